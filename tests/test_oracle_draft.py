@@ -1,0 +1,190 @@
+"""Pins for the Draft Attention oracle: hand-worked permutation, bijection,
+exact pooling/scoring cases, fp32 error bounds, and brute-force top-k."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from video_diffusion_transformer_lvsa_amd import synth
+
+
+def test_permutation_worked_example(golden_dir):
+    with open(os.path.join(golden_dir, "draft_perm_tiny.json")) as f:
+        g = json.load(f)
+    grid = oracle.draft_grid(g["T"], g["H"], g["W"], g["pool_h"], g["pool_w"])
+    perm, inv, bv = oracle.draft_permutation(grid)
+    assert perm.tolist() == g["perm"]
+    assert inv.tolist() == g["inv_perm"]
+    assert bv.tolist() == g["block_valid"]
+
+
+@pytest.mark.parametrize("T,H,W,ph,pw", [(33, 45, 80, 8, 16), (2, 5, 7, 2, 4), (3, 8, 16, 8, 16), (1, 1, 1, 1, 1)])
+def test_permutation_bijection(T, H, W, ph, pw):
+    g = oracle.draft_grid(T, H, W, ph, pw)
+    perm, inv, bv = oracle.draft_permutation(g)
+    valid = perm[perm >= 0]
+    assert len(valid) == g.N
+    assert np.array_equal(np.sort(valid), np.arange(g.N))
+    assert np.array_equal(perm[inv], np.arange(g.N))
+    # valid slots are a prefix of every block
+    pb = perm.reshape(g.nb, g.block_size)
+    for b in range(g.nb):
+        assert np.all(pb[b, : bv[b]] >= 0) and np.all(pb[b, bv[b]:] == -1)
+    # inverse restores order bitwise
+    x = np.arange(g.N * 3, dtype=np.int64).reshape(g.N, 3)
+    xp = np.where(perm[:, None] >= 0, x[np.maximum(perm, 0)], -7)
+    assert np.array_equal(xp[inv], x)
+
+
+def test_hunyuan_grid_counts():
+    g = oracle.draft_grid(33, 45, 80, 8, 16)
+    assert (g.Hp, g.Wp, g.nb, g.block_size, g.N_pad) == (48, 80, 990, 128, 126720)
+    _, _, bv = oracle.draft_permutation(g)
+    assert (bv == 128).sum() == 825 and (bv == 80).sum() == 165
+
+
+def _tile_mean_f64(x, g):
+    """Independent route: pad the [t, h, w] grid with NaN, reshape into tiles, nanmean in fp64."""
+    heads, n, d = x.shape
+    v = x.astype(np.float64).reshape(heads, g.T, g.H, g.W, d)
+    pad = np.full((heads, g.T, g.Hp, g.Wp, d), np.nan)
+    pad[:, :, : g.H, : g.W] = v
+    t = pad.reshape(heads, g.T, g.nbh, g.pool_h, g.nbw, g.pool_w, d).transpose(0, 1, 2, 4, 3, 5, 6)
+    t = t.reshape(heads, g.nb, g.block_size, d)
+    return np.nanmean(t, axis=2), np.sum(np.abs(np.nan_to_num(t)), axis=2)
+
+
+@pytest.mark.parametrize("T,H,W,ph,pw", [(2, 5, 7, 2, 4), (3, 12, 20, 8, 16)])
+def test_pool_matches_fp64_within_bound(T, H, W, ph, pw):
+    g = oracle.draft_grid(T, H, W, ph, pw)
+    rng = np.random.default_rng(0)
+    x = rng.standard_normal((2, g.N, 5)).astype(np.float32)
+    got = oracle.draft_pool(x, g)
+    mean64, abs_sum = _tile_mean_f64(x, g)
+    _, _, bv = oracle.draft_permutation(g)
+    n = bv[None, :, None].astype(np.float64)
+    u = 2.0 ** -24
+    bound = (n - 1) * u / (1 - (n - 1) * u) * abs_sum / n + np.abs(mean64) * 2 * u
+    assert np.all(np.abs(got.astype(np.float64) - mean64) <= bound + 1e-45)
+
+
+def test_pool_exact_on_representable_sums():
+    g = oracle.draft_grid(2, 12, 20, 8, 16)
+    rng = np.random.default_rng(1)
+    x = (rng.integers(-64, 64, size=(3, g.N, 4)) / 8.0).astype(np.float32)  # all partial sums exact in fp32
+    got = oracle.draft_pool(x, g)
+    mean64, _ = _tile_mean_f64(x, g)
+    _, _, bv = oracle.draft_permutation(g)
+    sums = mean64 * bv[None, :, None]
+    # fp64 division then fp32 rounding equals one correctly-rounded fp32 division (53 >= 2*24 + 2)
+    want = (sums / bv[None, :, None]).astype(np.float32)
+    assert np.array_equal(got, want)
+
+
+def test_pool_constant_tile():
+    g = oracle.draft_grid(1, 5, 7, 2, 4)
+    _, _, bv = oracle.draft_permutation(g)
+    perm, inv, _ = oracle.draft_permutation(g)
+    c = np.float32(0.1)
+    blk_val = np.float32(c) * np.arange(1, g.nb + 1, dtype=np.float32)
+    x = blk_val[inv // g.block_size][None, :, None].repeat(3, axis=2)
+    got = oracle.draft_pool(x, g)
+    # mean of n copies of one fp32 value: the sequential sum is exact only up to rounding,
+    # so compare with the bound; for power-of-two counts (4) with exact sums it is exact
+    for b in range(g.nb):
+        if bv[b] in (1, 2, 4):
+            assert np.all(got[0, b] == blk_val[b])
+        else:
+            assert np.allclose(got[0, b], blk_val[b], rtol=4e-7)
+
+
+def test_scores_exact_on_integers():
+    rng = np.random.default_rng(2)
+    q = rng.integers(-30, 30, size=(2, 9, 16)).astype(np.float32)
+    k = rng.integers(-30, 30, size=(2, 11, 16)).astype(np.float32)
+    got = oracle.draft_scores(q, k)
+    want = np.einsum("hic,hjc->hij", q.astype(np.int64), k.astype(np.int64))
+    assert np.array_equal(got, want.astype(np.float32))
+
+
+def test_scores_within_fp32_bound():
+    rng = np.random.default_rng(3)
+    q = rng.standard_normal((2, 13, 128)).astype(np.float32)
+    k = rng.standard_normal((2, 17, 128)).astype(np.float32)
+    got = oracle.draft_scores(q, k).astype(np.float64)
+    q64, k64 = q.astype(np.float64), k.astype(np.float64)
+    exact = np.einsum("hic,hjc->hij", q64, k64)
+    absd = np.einsum("hic,hjc->hij", np.abs(q64), np.abs(k64))
+    gam = 128 * 2.0 ** -24 / (1 - 128 * 2.0 ** -24)
+    assert np.all(np.abs(got - exact) <= gam * absd)
+
+
+def test_scores_no_fused_multiply_add():
+    """q = [1, 1+2^-12], k = [-1, 1+2^-12]: separate rounding gives 2^-11;
+    a fused multiply-add would keep the 2^-24 term of the product."""
+    e = 2.0 ** -12
+    q = np.array([[[1.0, 1.0 + e]]], dtype=np.float32)
+    k = np.array([[[-1.0, 1.0 + e]]], dtype=np.float32)
+    s = oracle.draft_scores(q, k)
+    assert s[0, 0, 0] == np.float32(2.0 ** -11)
+    assert s[0, 0, 0] != np.float32(2.0 ** -11 + 2.0 ** -24)
+
+
+def test_topk_count_rule():
+    assert oracle.topk_count(0.9, 990) == 99
+    assert math.ceil((1 - 0.9) * 990) == 99 and math.floor((1 - 0.9) * 990) == 98  # naive floor differs
+    assert oracle.topk_count(0.0, 10) == 10
+    assert oracle.topk_count(1.0, 10) == 1
+    assert oracle.topk_count(0.95, 7) == 1
+    assert oracle.topk_count(0.5, 5) == 3  # 2.5 + 0.5 -> 3
+
+
+def _brute_topk(row, k):
+    order = sorted(range(len(row)), key=lambda j: (-(float(row[j]) + 0.0), j))
+    return sorted(order[:k])
+
+
+def test_topk_brute_force():
+    rng = np.random.default_rng(4)
+    s = rng.integers(-3, 4, size=(2, 6, 23)).astype(np.float32)  # many ties
+    s[0, 0, :] = 0.0
+    s[0, 0, ::2] = -0.0
+    for k in (1, 3, 10, 23):
+        got = oracle.draft_topk(s, k)
+        for h in range(2):
+            for i in range(6):
+                assert got[h, i].tolist() == _brute_topk(s[h, i], k)
+    assert oracle.draft_topk(s, 5)[0, 0].tolist() == [0, 1, 2, 3, 4]  # all zero, -0 == +0 -> lowest indices
+
+
+def test_topk_known_sets():
+    row = np.array([[[5.0, 1.0, 9.0, 9.0, -2.0, 7.0]]], dtype=np.float32)
+    assert oracle.draft_topk(row, 1)[0, 0].tolist() == [2]
+    assert oracle.draft_topk(row, 2)[0, 0].tolist() == [2, 3]
+    assert oracle.draft_topk(row, 4)[0, 0].tolist() == [0, 2, 3, 5]
+
+
+def test_draft_mask_zero_inputs_select_first_blocks():
+    g = oracle.draft_grid(2, 5, 7, 2, 4)
+    z = np.zeros((2, g.N, 8), dtype=np.float32)
+    kv, cnt, _, _, s = oracle.draft_mask(z, z, g, 0.7)
+    k = oracle.topk_count(0.7, g.nb)
+    assert np.all(cnt == k)
+    assert np.all(kv == np.arange(k)[None, None, :])
+
+
+def test_draft_mask_end_to_end_small():
+    g = oracle.draft_grid(2, 10, 16, 4, 8)
+    q, k, _ = synth.video_qkv(11, 2, g.T, g.H, g.W, 32)
+    qf, kf = synth.bf16_to_f32(q), synth.bf16_to_f32(k)
+    kv, cnt, qb, kb, s = oracle.draft_mask(qf, kf, g, 0.5)
+    kk = oracle.topk_count(0.5, g.nb)
+    for h in range(2):
+        for i in range(g.nb):
+            assert kv[h, i].tolist() == _brute_topk(s[h, i], kk)
+    # the pooled map ranks the diagonal (a tile with itself) high for the shared smooth field
+    diag_rank = np.mean([i in kv[h, i] for h in range(2) for i in range(g.nb)])
+    assert diag_rank > 0.8
