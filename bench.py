@@ -1,0 +1,341 @@
+#!/usr/bin/env python3
+"""Benchmark of the block-sparse video-DiT attention path on one MI355X.
+
+Default workload: Wan-2.1-1.3B-shaped attention at 6x training length
+(T = 126 latent frames of 30x52 tokens, N = 196560, 12 heads, d = 128, bf16)
+with the LVSA frame mask (C = 21, W = 5, T_per = 8). One step = one pass of
+the path: build the LVSA mask for denoising step s (s advances every step)
+and run the block-sparse attention over it. Inputs are seeded synthetic
+tensors with the workload's shapes, resident in HBM before timing starts.
+
+Prints ONE JSON line. value = effective TFLOP/s over the timed steps,
+counting 4*d FLOP per visited (query, key) pair. The dense attention at the
+same shape is timed beside it for the sparse-vs-dense speedup, and the CPU
+oracle is timed on a bounded sample as a reported baseline.
+
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
+PEAK_HBM_GBS = 8000.0
+METRIC = "block-sparse attn ms/call + effective TFLOP/s (% bf16 MFMA peak), 1 MI355X"
+ATTN_SRC = os.path.join(ROOT, "video_diffusion_transformer_lvsa_amd", "csrc", "attn_bf16.hip")
+DRAFT_SRC = os.path.join(ROOT, "video_diffusion_transformer_lvsa_amd", "csrc", "draft.hip")
+
+WORKLOAD_NAMES = {
+    "wan1.3b-6x": "wan2.1-1.3b-6x-lvsa",
+    "wan1.3b-1x": "wan2.1-1.3b-1x-lvsa-full",
+    "wan14b-6x": "wan2.1-14b-6x-lvsa",
+    "hunyuan-draft": "hunyuanvideo-draft-90pct",
+}
+
+
+def src_hash(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def log(msg: str):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def lvsa_pairs(w, kv_cnt_host) -> int:
+    """Visited (query, key) pairs of one LVSA call, all heads."""
+    return int(w.heads) * w.P * w.P * int(kv_cnt_host.sum())
+
+
+def traffic_for(workload: str, kernel_src: str):
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary, if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_src_sha256_16") != src_hash(kernel_src):
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline_lvsa(w, q, k, v, budget_s: float):
+    """Time the fp64 oracle on whole query frames of the workload until ~budget_s."""
+    import numpy as np
+
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # threadpoolctl missing: report the affinity count
+        threads = len(os.sched_getaffinity(0))
+    idx, cnt = oracle.lvsa_mask(w.T, w.C, w.window, w.T_per, 0)
+    rng = np.random.default_rng(0)
+    frames = rng.permutation(w.T)
+    pairs = 0
+    t0 = time.perf_counter()
+    done = 0
+    for f in frames:
+        for h in range(w.heads):
+            rows = np.arange(f * w.P, (f + 1) * w.P)
+            oracle.block_sparse_attention(q, k, v, w.P, w.P, idx, cnt, rows=rows, heads=[h])
+            pairs += w.P * int(cnt[f]) * w.P
+            done += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    flops = 4.0 * w.d * pairs
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{done} (head, query-frame) pairs of 1560 rows x {w.C} frames of keys, LVSA s=0, fp64 numpy, "
+                  f"{dt:.1f} s",
+        "seconds": dt,
+        "ms_per_call_extrapolated": dt / pairs * (lvsa_pairs(w, cnt)) * 1e3,
+    }
+
+
+def run_lvsa(args, w):
+    import numpy as np
+    import torch
+
+    from video_diffusion_transformer_lvsa_amd import _lib, synth
+
+    log(f"generating inputs for {w.name}")
+    q, k, v = synth.video_qkv(w.seed, w.heads, w.T, w.H, w.W, w.d)
+    dev = torch.device("cuda:0")
+
+    def up(a):
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    dq, dk, dv = up(q), up(k), up(v)
+    o = torch.empty((w.heads, w.N, w.d), dtype=torch.float32, device=dev)
+    cap = max(_lib.lvsa_mask_capacity(w.T, w.C, w.window, w.T_per, s) for s in range(w.T_per))
+    kv_idx = torch.empty((w.T, cap), dtype=torch.int32, device=dev)
+    kv_cnt = torch.empty((w.T,), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        _lib.lvsa_mask(w.T, w.C, w.window, w.T_per, i % w.T_per, cap=cap, kv_idx=kv_idx, kv_cnt=kv_cnt)
+        _lib.block_sparse_attn_fwd(dq, dk, dv, w.P, w.P, kv_idx, kv_cnt, out=o)
+
+    log("warmup")
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    pairs = []
+    for s in range(w.T_per):
+        _lib.lvsa_mask(w.T, w.C, w.window, w.T_per, s, cap=cap, kv_idx=kv_idx, kv_cnt=kv_cnt)
+        pairs.append(lvsa_pairs(w, kv_cnt.cpu().numpy()))
+    torch.cuda.synchronize()
+
+    log(f"timing {args.steps} steps")
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    total_pairs = 0
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(args.steps):
+        s = (args.warmup + i) % w.T_per
+        _lib.lvsa_mask(w.T, w.C, w.window, w.T_per, s, cap=cap, kv_idx=kv_idx, kv_cnt=kv_cnt)
+        ev[i][0].record(stream)
+        _lib.block_sparse_attn_fwd(dq, dk, dv, w.P, w.P, kv_idx, kv_cnt, out=o)
+        ev[i][1].record(stream)
+        total_pairs += pairs[s]
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_total = t0.elapsed_time(t1)
+    attn_ms = [a.elapsed_time(b) for a, b in ev]
+    ms_per_step = ms_total / args.steps
+    flops_total = 4.0 * w.d * total_pairs
+    value = flops_total / (ms_total * 1e-3) / 1e12
+    attn_avg = sum(attn_ms) / len(attn_ms)
+    flop_per_launch = flops_total / args.steps
+    achieved = flop_per_launch / (attn_avg * 1e-3) / 1e12
+    mask_ms = ms_per_step - attn_avg
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": WORKLOAD_NAMES[w.name],
+            "T": w.T, "H": w.H, "W": w.W, "tokens": w.N, "heads": w.heads, "d": w.d,
+            "C": w.C, "window": w.window, "T_per": w.T_per, "steps_s": "s = step mod T_per",
+            "flop_per_call": flop_per_launch,
+        },
+        "attn_ms_per_call": round(attn_avg, 4),
+        "attn_ms_min": round(min(attn_ms), 4),
+        "mask_build_ms": round(max(mask_ms, 0.0), 4),
+        "pct_bf16_peak": round(100.0 * achieved / PEAK_BF16_TFLOPS, 2),
+    }
+    res["roofline"] = {
+        "bound": "mfma",
+        "achieved": round(achieved, 2),
+        "peak": PEAK_BF16_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+        "traffic": traffic_for(w.name, ATTN_SRC),
+        "kernel": "bsa_fwd_bf16_kernel<128,64>",
+    }
+
+    if not args.no_dense:
+        log("timing dense attention at the same shape")
+        _lib.dense_attn_fwd(dq, dk, dv, out=o)
+        torch.cuda.synchronize()
+        d0 = torch.cuda.Event(enable_timing=True)
+        d1 = torch.cuda.Event(enable_timing=True)
+        nd = args.dense_steps
+        d0.record(stream)
+        for _ in range(nd):
+            _lib.dense_attn_fwd(dq, dk, dv, out=o)
+        d1.record(stream)
+        torch.cuda.synchronize()
+        dense_ms = d0.elapsed_time(d1) / nd
+        dense_flops = 4.0 * w.d * w.heads * float(w.N) * w.N
+        res["dense_ms_per_call"] = round(dense_ms, 3)
+        res["dense_tflops"] = round(dense_flops / (dense_ms * 1e-3) / 1e12, 2)
+        res["speedup_vs_dense"] = round(dense_ms / attn_avg, 3)
+
+    if not args.no_cpu_baseline:
+        log(f"timing the CPU oracle for ~{args.cpu_seconds} s")
+        res["cpu_baseline"] = cpu_baseline_lvsa(w, q, k, v, args.cpu_seconds)
+    return res
+
+
+def run_draft(args, w):
+    import numpy as np
+    import torch
+
+    from video_diffusion_transformer_lvsa_amd import _lib, synth
+
+    log(f"generating inputs for {w.name}")
+    q, k, v = synth.video_qkv(w.seed, w.heads, w.T, w.H, w.W, w.d)
+    dev = torch.device("cuda:0")
+
+    def up(a):
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    dq, dk, dv = up(q), up(k), up(v)
+    bs = w.pool_h * w.pool_w
+    stream = torch.cuda.current_stream()
+
+    def step():
+        out = _lib.draft_mask_and_perm(dq, dk, dv, w.T, w.H, w.W, w.pool_h, w.pool_w, w.sparsity)
+        op = _lib.block_sparse_attn_fwd(out["q_perm"], out["k_perm"], out["v_perm"], bs, bs, out["kv_idx"],
+                                        out["kv_cnt"], mask_heads=w.heads, block_valid=out["block_valid"])
+        o = _lib.token_permute(op, out["inv_perm"])
+        return out, op, o
+
+    for _ in range(args.warmup):
+        out, op, o = step()
+    torch.cuda.synchronize()
+    kv = out["kv_idx"].cpu().numpy()
+    bv = out["block_valid"].cpu().numpy().astype(np.int64)
+    pairs = int(sum((bv * bv[kv[h]].sum(axis=1)).sum() for h in range(w.heads)))
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+    times = {"mask": [], "attn": [], "scatter": []}
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(args.steps):
+        e[0].record(stream)
+        out = _lib.draft_mask_and_perm(dq, dk, dv, w.T, w.H, w.W, w.pool_h, w.pool_w, w.sparsity)
+        e[1].record(stream)
+        op = _lib.block_sparse_attn_fwd(out["q_perm"], out["k_perm"], out["v_perm"], bs, bs, out["kv_idx"],
+                                        out["kv_cnt"], mask_heads=w.heads, block_valid=out["block_valid"])
+        e[2].record(stream)
+        _lib.token_permute(op, out["inv_perm"])
+        e[3].record(stream)
+        torch.cuda.synchronize()
+        times["mask"].append(e[0].elapsed_time(e[1]))
+        times["attn"].append(e[1].elapsed_time(e[2]))
+        times["scatter"].append(e[2].elapsed_time(e[3]))
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_total = t0.elapsed_time(t1)
+    attn_avg = sum(times["attn"]) / len(times["attn"])
+    flops = 4.0 * w.d * pairs
+    res = {
+        "metric": METRIC,
+        "value": round(flops * args.steps / (ms_total * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_total / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD_NAMES[w.name], "T": w.T, "H": w.H, "W": w.W, "heads": w.heads, "d": w.d,
+                   "pool": [w.pool_h, w.pool_w], "sparsity": w.sparsity, "flop_per_call": flops},
+        "stage_ms": {k2: round(sum(v2) / len(v2), 4) for k2, v2 in times.items()},
+        "roofline": {"bound": "mfma", "achieved": round(flops / (attn_avg * 1e-3) / 1e12, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(flops / (attn_avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic_for(w.name, ATTN_SRC), "kernel": "bsa_fwd_bf16_kernel<128,64>"},
+    }
+    return res
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=16)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="wan1.3b-6x", choices=sorted(WORKLOAD_NAMES))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--dense-steps", type=int, default=3)
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (attention shards by heads with "
+              "no exchange; see the design notes). Run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from video_diffusion_transformer_lvsa_amd import _lib, synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    _lib.load()
+    w = synth.WORKLOADS[args.workload]
+    res = run_draft(args, w) if w.kind == "draft" else run_lvsa(args, w)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,189 @@
+/*
+ * lvsa.h -- C ABI of liblvsa.so: block-sparse softmax attention for video
+ * diffusion transformers on AMD Instinct MI355X (gfx950), with the two mask
+ * builders it runs on (LVSA and Draft Attention) and a dense baseline.
+ *
+ * Sources (cited by page title and section):
+ *   [LVSA]  "LVSA: Training-Free Sparse Attention for Long Video Diffusion"
+ *           (gist.science explainer), technical summary §1 "Problem
+ *           statement", §2 "Methodology" (core mechanism, complexity).
+ *   [DRAFT] "科学家提出视频扩散模型加速方法，在H100实现一倍以上端到端加速"
+ *           (163.com article on Draft Attention): [t,h,w] reshape, average
+ *           pooling into a draft map, sparse mask, pool_h*pool_w = block_size,
+ *           reorder into contiguous blocks.
+ *
+ * Conventions shared by every call
+ *   - Tensors Q, K, V, O are [heads, n, d], row-major, contiguous, batch 1.
+ *     Tokens are frame-major over the [t, h, w] grid: n = (t*H + y)*W + x.
+ *   - d is 64 or 128. dtype LVSA_BF16 (bfloat16 bits) or LVSA_F32.
+ *     O is always fp32.
+ *   - Every pointer argument is a device pointer (memory the caller
+ *     allocated with hipMalloc or a framework allocator) unless marked
+ *     "host". Device pointers must be 16-byte aligned. The caller owns every
+ *     buffer, including workspaces; the library keeps no device memory and
+ *     no pointers between calls.
+ *   - stream is a hipStream_t passed as void* (NULL = the default stream).
+ *     All device work is enqueued asynchronously on it; outputs are valid
+ *     once the stream has been synchronised.
+ *   - Return value: LVSA_OK (0) or a negative lvsa_status. Arguments are
+ *     validated on the host before anything is launched; on error nothing
+ *     is launched and lvsa_last_error() describes the failure. No C++
+ *     exception crosses this boundary. Calls are thread-safe (the error text
+ *     is thread-local).
+ *   - Device-side index data (kv_idx, kv_cnt, block_valid) cannot be checked
+ *     on the host: kernels clamp kv_cnt to max_kv, skip list entries outside
+ *     [0, number of KV blocks) and clamp block_valid to [0, block size], so a
+ *     bad list never causes an out-of-bounds access.
+ */
+#ifndef LVSA_H
+#define LVSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LVSA_OK = 0,
+  LVSA_EINVAL = -1,      /* an argument is invalid (shape, pointer, parameter) */
+  LVSA_ERANGE = -2,      /* an output capacity is too small */
+  LVSA_EDEVICE = -3,     /* no usable GPU, or a HIP launch/runtime error */
+  LVSA_ENOMEM = -4,      /* workspace too small */
+  LVSA_EUNSUPPORTED = -5 /* valid request outside what the kernels implement */
+} lvsa_status;
+
+typedef enum { LVSA_F32 = 0, LVSA_BF16 = 1 } lvsa_dtype;
+
+/* Text of the calling thread's last failure ("" if none). Host pointer owned
+ * by the library, valid until the thread's next call. */
+const char* lvsa_last_error(void);
+
+/* Library version string (host pointer, static). */
+const char* lvsa_version(void);
+
+/* ------------------------------------------------------------------------
+ * LVSA frame mask  [LVSA §2 "Core mechanism"]
+ *
+ * Query frame t (0 <= t < T) attends to A(t) = G_s ∪ W(t):
+ *   G_s  = { f in [0,T) : f ≡ step (mod T_per) }   rotating global anchors;
+ *          over T_per consecutive steps every frame is an anchor exactly once.
+ *   W(t) = the first k frames in the order of the key (|f - t|, f): a window
+ *          centred on t, the earlier frame first on ties, shifted inward at the
+ *          ends. k starts at `window` and grows one frame at a time while
+ *          |A(t)| < min(C, T) and k < T (the expanding window keeps |A(t)| at
+ *          the budget C). If the anchors plus the base window already exceed C
+ *          the set is kept whole.
+ * ------------------------------------------------------------------------ */
+
+/* Host-only. Exact max over t of |A(t)| for these parameters (>= 1), or a
+ * negative lvsa_status. Use it as `cap` for lvsa_mask. Requires T >= 1,
+ * C >= 1, window >= 1, T_per >= 1, step >= 0. */
+int lvsa_mask_capacity(int T, int C, int window, int T_per, int step);
+
+/* Writes kv_idx [T, cap] int32 (frames of A(t) ascending, then -1 padding)
+ * and kv_cnt [T] int32 (= |A(t)|). Both are device buffers owned by the
+ * caller. LVSA_ERANGE if cap < lvsa_mask_capacity(...). The mask is the same
+ * for every head and layer of one denoising step. */
+int lvsa_mask(int T, int C, int window, int T_per, int step, int32_t* kv_idx, int32_t* kv_cnt, int cap,
+              void* stream);
+
+/* ------------------------------------------------------------------------
+ * Draft Attention mask builder and reorder  [DRAFT]
+ *
+ * Grid [T, H, grid_w] tokens; tiles of pool_h x pool_w tokens (block size
+ * bs = pool_h*pool_w). The grid is padded at the bottom/right to multiples of
+ * the tile: Hp = ceil(H/pool_h)*pool_h, Wp likewise; nb = T*(Hp/pool_h)*(Wp/pool_w)
+ * blocks in raster order (t, hb, wb); N_pad = nb*bs.
+ *   perm[p]        (p < N_pad)  original token at reordered slot p, -1 for a pad;
+ *                  within a block the valid tokens come first, in (hi, wi) order.
+ *   inv_perm[n]    (n < T*H*grid_w)  reordered slot of token n.
+ *   block_valid[b] number of valid tokens of block b (they are its first slots).
+ * Pooling: for each head, block and channel c, acc = +0.0f, then acc += x for
+ *   each valid token in slot order (each add rounded to fp32), mean = acc/count
+ *   (one IEEE fp32 division). Applied to Q and to K.
+ * Draft map: s[h,i,j] = fold over c = 0..d-1 of acc = fl(acc + fl(q̄[i,c]*k̄[j,c]))
+ *   starting from +0.0f, no fused multiply-add (the unscaled logit: softmax and
+ *   1/sqrt(d) do not change a row's ranking).
+ * Top-k: each row keeps k = clamp(floor((1 - sparsity)*nb + 0.5), 1, nb) blocks,
+ *   larger score first, lower block index first on a tie, -0 equal to +0,
+ *   stored in ascending block order. Scores must be finite.
+ * ------------------------------------------------------------------------ */
+
+/* Host-only. Grid facts: *nb, *n_pad, *block_size, *k (for this sparsity).
+ * Any output pointer may be NULL. Returns LVSA_OK or LVSA_EINVAL. */
+int draft_grid_info(int T, int H, int grid_w, int pool_h, int pool_w, double sparsity, int* nb, int* n_pad,
+                    int* block_size, int* k);
+
+/* Host-only. Bytes of device workspace draft_mask_and_perm needs:
+ * pooled Q̄ and K̄, each [heads, nb, d] fp32, at byte offsets 0 and
+ * heads*nb*d*4. Returns 0 for invalid arguments. */
+size_t draft_workspace_bytes(int heads, int T, int H, int grid_w, int d, int pool_h, int pool_w);
+
+/* Full Draft mask builder on Q, K (and the reorder of Q, K, V).
+ *   q, k, v     [heads, T*H*grid_w, d] of dtype dt (v may be NULL when v_perm is NULL)
+ *   kv_idx      out [heads, nb, k] int32 (k from draft_grid_info)
+ *   kv_cnt      out [heads, nb] int32 (= k)
+ *   perm        out [N_pad] int32; inv_perm out [T*H*grid_w] int32; block_valid out [nb] int32
+ *   q_perm, k_perm, v_perm  out [heads, N_pad, d] of dtype dt: the reordered
+ *               tensors, pads zero. All three NULL to skip the reorder.
+ *   workspace   device buffer of ws_bytes >= draft_workspace_bytes(...);
+ *               holds Q̄ and K̄ on return (layout above).
+ * Requires block size <= 1024 and nb <= 4096. */
+int draft_mask_and_perm(const void* q, const void* k, const void* v, int dt, int heads, int T, int H, int grid_w,
+                        int d, int pool_h, int pool_w, double sparsity, int32_t* kv_idx, int32_t* kv_cnt,
+                        int32_t* perm, int32_t* inv_perm, int32_t* block_valid, void* q_perm, void* k_perm,
+                        void* v_perm, void* workspace, size_t ws_bytes, void* stream);
+
+/* The draft map itself, materialised: scores [heads, nb_q, nb_k] fp32 from
+ * q̄ [heads, nb_q, d] and k̄ [heads, nb_k, d] fp32, same fixed arithmetic as
+ * above. For inspection and testing; draft_mask_and_perm never stores it. */
+int draft_scores(const float* qbar, const float* kbar, int heads, int nb_q, int nb_k, int d, float* scores,
+                 void* stream);
+
+/* Row gather: dst[h, i, :] = src[h, dst_to_src[i], :], or zeros where
+ * dst_to_src[i] < 0 or >= n_src. src [heads, n_src, d], dst [heads, n_dst, d],
+ * element type dt (bf16 or fp32); the map is [n_dst] int32. With
+ * dst_to_src = inv_perm it scatters a reordered O back to token order; with
+ * perm it builds a reordered tensor. src and dst must not overlap. */
+int token_permute(const void* src, void* dst, int dt, int heads, int n_src, int n_dst, int d,
+                  const int32_t* dst_to_src, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Attention  [LVSA §1 "Problem statement" (dense), §2 "Complexity"
+ * (frame-block-sparse); DRAFT (block-sparse on the reordered tokens)]
+ *
+ * Query row i of head h belongs to query block qb = i / block_q. Its keys
+ * are the valid rows of the KV blocks kv_idx[hm][qb][0 .. kv_cnt[hm][qb]-1],
+ * hm = (mask_heads > 1 ? h : 0): block b holds rows
+ * [b*block_k, b*block_k + valid(b)) ∩ [0, n), valid(b) = block_valid[b] if
+ * block_valid is non-NULL, else block_k. With block_valid, query rows at a
+ * slot >= block_valid[qb] are pads: their output rows are 0 (requires
+ * block_q == block_k). A query with no keys gets output 0.
+ *   O[h,i,:] = sum_j exp(s_ij - m_i) V[h,j,:] / sum_j exp(s_ij - m_i),
+ *   s_ij = scale * <Q[h,i,:], K[h,j,:]>, m_i = max_j s_ij   (not causal).
+ * bf16: QKᵀ and PV on bf16 MFMA with fp32 accumulation; probabilities are
+ * rounded to bf16 for the PV product and the row sum uses those same rounded
+ * values. fp32: fp32 arithmetic throughout. O is fp32 [heads, n, d].
+ *
+ * LVSA:  block_q = block_k = P (tokens per frame), mask_heads = 1, kv_idx =
+ *        the lvsa_mask output (cap = max_kv), block_valid = NULL.
+ * Draft: block_q = block_k = pool_h*pool_w on q_perm/k_perm/v_perm,
+ *        mask_heads = heads, block_valid from draft_mask_and_perm; then
+ *        token_permute(O_perm -> O, inv_perm).
+ * ------------------------------------------------------------------------ */
+int block_sparse_attn_fwd(const void* q, const void* k, const void* v, float* o, int dt, int heads, int n, int d,
+                          int block_q, int block_k, const int32_t* kv_idx, const int32_t* kv_cnt, int max_kv,
+                          int mask_heads, const int32_t* block_valid, float scale, void* stream);
+
+/* Dense baseline: every query attends to all n keys. Same arithmetic and
+ * layout as block_sparse_attn_fwd. */
+int dense_attn_fwd(const void* q, const void* k, const void* v, float* o, int dt, int heads, int n, int d,
+                   float scale, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LVSA_H */

@@ -53,15 +53,15 @@ def _chunks(rows: np.ndarray, size: int):
 
 def dense_attention(q, k, v, scale: float | None = None, rows=None, heads=None, chunk: int = 512) -> np.ndarray:
     """Dense attention; q, k, v [heads, N, d] (bf16 bits or float). Returns fp64 [len(heads), len(rows), d]."""
-    q64, k64, v64 = to_f64(q), to_f64(k), to_f64(v)
-    H, n, d = q64.shape
+    H, n, d = q.shape
     scale = 1.0 / np.sqrt(d) if scale is None else scale
     rows = np.arange(n) if rows is None else np.asarray(rows)
     heads = list(range(H)) if heads is None else list(heads)
     out = np.zeros((len(heads), len(rows), d), dtype=np.float64)
     for hi, h in enumerate(heads):
+        kh, vh = to_f64(k[h]), to_f64(v[h])
         for ci, r in enumerate(_chunks(rows, chunk)):
-            out[hi, ci * chunk : ci * chunk + len(r)] = attention_keyset(q64[h, r], k64[h], v64[h], scale)
+            out[hi, ci * chunk : ci * chunk + len(r)] = attention_keyset(to_f64(q[h, r]), kh, vh, scale)
     return out
 
 
@@ -87,8 +87,7 @@ def block_sparse_attention(q, k, v, block_q: int, block_k: int, kv_idx, kv_cnt, 
     [b*block_k, b*block_k + valid(b)) inside [0, n), valid(b) = block_valid[b]
     or block_k). A query row at a slot >= block_valid of its block is a pad
     and gets output 0. Returns fp64 [len(heads), len(rows), d]."""
-    q64, k64, v64 = to_f64(q), to_f64(k), to_f64(v)
-    H, n, d = q64.shape
+    H, n, d = q.shape
     scale = 1.0 / np.sqrt(d) if scale is None else scale
     kv_idx = np.asarray(kv_idx)
     kv_cnt = np.asarray(kv_cnt)
@@ -110,31 +109,33 @@ def block_sparse_attention(q, k, v, block_q: int, block_k: int, kv_idx, kv_cnt, 
             if len(r) == 0:
                 continue
             keys = _block_keys(kv_idx[hm, qb, : int(kv_cnt[hm, qb])], block_k, n, block_valid)
-            out[hi, sel] = attention_keyset(q64[h, r], k64[h, keys], v64[h, keys], scale)
+            out[hi, sel] = attention_keyset(to_f64(q[h, r]), to_f64(k[h, keys]), to_f64(v[h, keys]), scale)
     return out
 
 
 def draft_attention_original_order(q, k, v, perm, inv_perm, block_valid, block_size: int, kv_idx, kv_cnt,
-                                   scale: float | None = None, heads=None) -> np.ndarray:
+                                   scale: float | None = None, heads=None, rows=None) -> np.ndarray:
     """Draft block-sparse attention computed directly in the original token order.
 
     Token n sits in block b = inv_perm[n] // block_size of the reorder; its keys
     are the original tokens perm[b'*block_size + o] for every listed block b'
     and every valid slot o < block_valid[b']. No reordered tensor is built, so
     comparing this with reorder -> block-sparse attention -> inverse reorder
-    checks that the reorder does not change the result."""
-    q64, k64, v64 = to_f64(q), to_f64(k), to_f64(v)
-    H, n, d = q64.shape
+    checks that the reorder does not change the result.
+    Returns fp64 [len(heads), len(rows), d] (rows = original token indices,
+    default all)."""
+    H, n, d = q.shape
     scale = 1.0 / np.sqrt(d) if scale is None else scale
     heads = list(range(H)) if heads is None else list(heads)
-    nb = len(block_valid)
-    out = np.zeros((len(heads), n, d), dtype=np.float64)
+    rows = np.arange(n) if rows is None else np.asarray(rows)
+    assert np.all(inv_perm >= 0)
+    qblk = np.asarray(inv_perm)[rows] // block_size
+    out = np.zeros((len(heads), len(rows), d), dtype=np.float64)
     for hi, h in enumerate(heads):
-        for b in range(nb):
-            qrows = perm[b * block_size : b * block_size + int(block_valid[b])]
+        for b in np.unique(qblk):
+            sel = np.nonzero(qblk == b)[0]
             keys = np.concatenate(
                 [perm[bb * block_size : bb * block_size + int(block_valid[bb])] for bb in kv_idx[h, b, : int(kv_cnt[h, b])]]
             )
-            out[hi, qrows] = attention_keyset(q64[h, qrows], k64[h, keys], v64[h, keys], scale)
-    assert np.all(inv_perm >= 0)
+            out[hi, sel] = attention_keyset(to_f64(q[h, rows[sel]]), to_f64(k[h, keys]), to_f64(v[h, keys]), scale)
     return out

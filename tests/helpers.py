@@ -1,0 +1,66 @@
+"""Shared helpers for the GPU parity tests (host-side marshalling and comparisons)."""
+import sys
+
+import numpy as np
+
+# Attention tolerance for bf16 inputs with fp32 accumulation, against fp64.
+MAX_ABS = 1e-2
+REL_L2 = 5e-3
+
+
+def note(msg: str):
+    """Name the case about to run on the GPU (flushed, so a crash leaves it behind)."""
+    print(f"[case] {msg}", file=sys.stderr, flush=True)
+
+
+def to_dev_bf16(a: np.ndarray):
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def to_dev(a: np.ndarray):
+    import torch
+
+    if a.dtype == np.uint16:
+        return to_dev_bf16(a)
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def to_host(t) -> np.ndarray:
+    import torch
+
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+def attn_errors(got: np.ndarray, ref: np.ndarray):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    err = np.abs(got - ref)
+    max_abs = float(err.max()) if err.size else 0.0
+    nref = float(np.linalg.norm(ref))
+    rel = float(np.linalg.norm(got - ref) / nref) if nref > 0 else float(np.linalg.norm(got - ref))
+    return max_abs, rel
+
+
+def assert_attn_close(got, ref, max_abs=MAX_ABS, rel_l2=REL_L2, what=""):
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    m, r = attn_errors(got, ref)
+    assert m <= max_abs and r <= rel_l2, f"{what}: max-abs {m:.3e} (bound {max_abs}), rel-L2 {r:.3e} (bound {rel_l2})"
+    return m, r
+
+
+def sample_frame_rows(rng, T: int, P: int, nframes: int = 6, per_frame: int = 96):
+    """Query rows for sampled parity at full size: the first, second, middle and
+    last frames plus random ones; in each, the first 32 rows, the last 32 rows
+    (the ragged tail of a frame) and random rows."""
+    frames = sorted(set([0, 1, T // 2, T - 1] + list(rng.choice(T, size=max(0, nframes - 4), replace=False))))
+    rows = []
+    for f in frames:
+        base = f * P
+        loc = set(range(min(32, P))) | set(range(max(0, P - 32), P))
+        loc |= set(rng.choice(P, size=min(P, max(0, per_frame - len(loc))), replace=False).tolist())
+        rows.extend(base + np.array(sorted(loc)))
+    return np.array(rows, dtype=np.int64)

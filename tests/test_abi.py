@@ -1,0 +1,139 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function the
+header declares, validates arguments before any launch, and its host-only
+helpers agree with the oracle."""
+import ctypes
+
+import numpy as np
+import pytest
+
+import oracle
+from video_diffusion_transformer_lvsa_amd import _lib
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def _no_gpu():
+    import torch
+
+    return torch.cuda.device_count() == 0
+
+
+def test_exports_every_declared_function(lib):
+    names = _lib.header_functions()
+    for required in ("lvsa_mask", "draft_mask_and_perm", "block_sparse_attn_fwd", "dense_attn_fwd"):
+        assert required in names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(_lib.SIGNATURES)
+    assert lib.lvsa_version().decode().startswith("lvsa")
+
+
+@pytest.mark.parametrize("T,C,W,T_per,s", [(4, 3, 2, 2, 0), (126, 21, 5, 8, 0), (126, 21, 5, 8, 7), (21, 21, 5, 8, 3),
+                                           (8, 3, 4, 3, 0), (6, 2, 3, 1, 0), (1, 1, 1, 1, 0), (13, 40, 2, 5, 9)])
+def test_capacity_matches_oracle(lib, T, C, W, T_per, s):
+    assert lib.lvsa_mask_capacity(T, C, W, T_per, s) == oracle.lvsa_capacity(T, C, W, T_per, s)
+
+
+def test_capacity_sweep(lib):
+    for T in (1, 3, 7, 12):
+        for C in (1, 4, 9):
+            for W in (1, 3):
+                for T_per in (1, 2, 5):
+                    for s in (0, 3):
+                        assert lib.lvsa_mask_capacity(T, C, W, T_per, s) == oracle.lvsa_capacity(T, C, W, T_per, s)
+
+
+@pytest.mark.parametrize("args", [(0, 3, 2, 2, 0), (4, 0, 2, 2, 0), (4, 3, 0, 2, 0), (4, 3, 2, 0, 0), (4, 3, 2, 2, -1)])
+def test_capacity_rejects(lib, args):
+    assert lib.lvsa_mask_capacity(*args) == _lib.LVSA_EINVAL
+    assert _lib.last_error()
+
+
+@pytest.mark.parametrize("T,H,W,ph,pw,sp", [(33, 45, 80, 8, 16, 0.9), (2, 5, 7, 2, 4, 0.5), (1, 3, 4, 2, 2, 0.0),
+                                            (3, 8, 16, 8, 16, 1.0)])
+def test_grid_info_matches_oracle(lib, T, H, W, ph, pw, sp):
+    info = _lib.draft_grid_info(T, H, W, ph, pw, sp)
+    g = oracle.draft_grid(T, H, W, ph, pw)
+    assert info == {"nb": g.nb, "n_pad": g.N_pad, "block_size": g.block_size, "k": oracle.topk_count(sp, g.nb)}
+    assert _lib.draft_workspace_bytes(24, T, H, W, 128, ph, pw) == 2 * 24 * g.nb * 128 * 4
+
+
+def test_grid_info_rejects(lib):
+    with pytest.raises(_lib.LvsaError):
+        _lib.draft_grid_info(0, 3, 4, 2, 2, 0.5)
+    with pytest.raises(_lib.LvsaError):
+        _lib.draft_grid_info(1, 3, 4, 2, 2, 1.5)
+    with pytest.raises(_lib.LvsaError) as e:
+        _lib.draft_grid_info(1, 64, 64, 64, 32, 0.5)  # block size 2048
+    assert e.value.code == _lib.LVSA_EUNSUPPORTED
+
+
+FAKE = ctypes.c_void_p(1 << 20)  # aligned, never dereferenced: every call below fails validation first
+MIS = ctypes.c_void_p((1 << 20) + 4)
+
+
+def test_attention_validation(lib):
+    f = lib.block_sparse_attn_fwd
+    ok = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, dt=1, heads=2, n=256, d=128, bq=64, bk=64, idx=FAKE, cnt=FAKE, max_kv=4,
+              mh=1, bv=None, scale=0.088)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["q"], a["k"], a["v"], a["o"], a["dt"], a["heads"], a["n"], a["d"], a["bq"], a["bk"], a["idx"],
+                 a["cnt"], a["max_kv"], a["mh"], a["bv"], a["scale"], None)
+
+    assert call(d=96) == _lib.LVSA_EUNSUPPORTED
+    assert call(dt=7) == _lib.LVSA_EINVAL
+    assert call(q=None) == _lib.LVSA_EINVAL
+    assert call(k=MIS) == _lib.LVSA_EINVAL
+    assert call(bq=0) == _lib.LVSA_EINVAL
+    assert call(mh=3) == _lib.LVSA_EINVAL
+    assert call(max_kv=-1) == _lib.LVSA_EINVAL
+    assert call(cnt=None) == _lib.LVSA_EINVAL
+    assert call(bv=FAKE, bk=32) == _lib.LVSA_EINVAL
+    assert call(scale=float("inf")) == _lib.LVSA_EINVAL
+    assert call(n=1 << 25) == _lib.LVSA_EINVAL  # n*d >= 2^31
+    # empty problems are valid no-ops
+    assert call(heads=0) == 0
+    assert call(n=0) == 0
+    g = lib.dense_attn_fwd
+    assert g(FAKE, FAKE, FAKE, FAKE, 1, 2, 256, 100, 0.1, None) == _lib.LVSA_EUNSUPPORTED
+    assert g(FAKE, FAKE, FAKE, None, 1, 2, 256, 128, 0.1, None) == _lib.LVSA_EINVAL
+    assert g(FAKE, FAKE, FAKE, FAKE, 1, 0, 256, 128, 0.1, None) == 0
+
+
+def test_mask_and_permute_validation(lib):
+    assert lib.lvsa_mask(126, 21, 5, 8, 0, FAKE, FAKE, 20, None) == _lib.LVSA_ERANGE
+    assert "required 21" in _lib.last_error()
+    assert lib.lvsa_mask(126, 21, 5, 8, 0, None, FAKE, 21, None) == _lib.LVSA_EINVAL
+    assert lib.lvsa_mask(0, 21, 5, 8, 0, FAKE, FAKE, 21, None) == _lib.LVSA_EINVAL
+    tp = lib.token_permute
+    assert tp(FAKE, FAKE, 1, 2, 10, 10, 12, FAKE, None) == _lib.LVSA_EUNSUPPORTED  # 24-byte rows
+    assert tp(FAKE, FAKE, 1, 2, 10, 10, 128, None, None) == _lib.LVSA_EINVAL
+    assert tp(FAKE, FAKE, 1, 2, 10, 10, 128, FAKE, None) == _lib.LVSA_EINVAL  # overlap
+    assert tp(FAKE, FAKE, 1, 2, 10, 0, 128, FAKE, None) == 0
+    dm = lib.draft_mask_and_perm
+    base = [FAKE, FAKE, FAKE, 1, 2, 2, 10, 16, 128, 4, 8, 0.5, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE]
+    need = lib.draft_workspace_bytes(2, 2, 10, 16, 128, 4, 8)
+    assert dm(*base, FAKE, need - 4, None) == _lib.LVSA_ENOMEM
+    bad = list(base)
+    bad[18] = None  # k_perm NULL but q_perm set
+    assert dm(*bad, FAKE, need, None) == _lib.LVSA_EINVAL
+    bad = list(base)
+    bad[8] = 80
+    assert dm(*bad, FAKE, need, None) == _lib.LVSA_EUNSUPPORTED
+    bad = list(base)
+    bad[11] = -0.1
+    assert dm(*bad, FAKE, need, None) == _lib.LVSA_EINVAL
+    ds = lib.draft_scores
+    assert ds(FAKE, FAKE, 1, 2, 3, 0, FAKE, None) == _lib.LVSA_EINVAL
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="checks the no-device error path")
+def test_no_device_is_reported(lib):
+    assert lib.lvsa_mask(4, 3, 2, 2, 0, FAKE, FAKE, 3, None) == _lib.LVSA_EDEVICE
+    assert "GPU" in _lib.last_error()
+    assert lib.dense_attn_fwd(FAKE, FAKE, FAKE, FAKE, 1, 2, 256, 128, 0.1, None) == _lib.LVSA_EDEVICE

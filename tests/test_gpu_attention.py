@@ -1,0 +1,295 @@
+"""GPU parity of block-sparse and dense attention against the fp64 oracle.
+
+Small problems are compared on every row; the full-size workloads (Wan-1.3B
+at 1x and 6x length, HunyuanVideo Draft, Wan-14B at 6x) on seeded sampled
+rows, in the launch configuration the benchmark times."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from video_diffusion_transformer_lvsa_amd import _lib, synth
+
+from helpers import assert_attn_close, note, sample_frame_rows, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _lvsa_case(q, k, v, T, P, C, W, T_per, s, rows=None, heads=None, tol=None):
+    torch = _torch()
+    note(f"lvsa attention T={T} P={P} C={C} W={W} T_per={T_per} s={s} heads={q.shape[0]} d={q.shape[2]} "
+         f"dtype={q.dtype}")
+    idx, cnt = _lib.lvsa_mask(T, C, W, T_per, s)
+    o = _lib.block_sparse_attn_fwd(to_dev(q), to_dev(k), to_dev(v), P, P, idx, cnt)
+    torch.cuda.synchronize()
+    want_idx, want_cnt = oracle.lvsa_mask(T, C, W, T_per, s)
+    ref = oracle.block_sparse_attention(q, k, v, P, P, want_idx, want_cnt, rows=rows, heads=heads)
+    got = to_host(o)
+    if heads is not None:
+        got = got[heads]
+    if rows is not None:
+        got = got[:, rows]
+    return got, ref
+
+
+@pytest.mark.parametrize("s", [0, 1, 2, 3])
+def test_tiny_fp32_lvsa(s):
+    w = synth.WORKLOADS["tiny"]
+    q, k, v = synth.iid_qkv(w.seed, w.heads, w.N, w.d)
+    got, ref = _lvsa_case(q, k, v, w.T, w.P, w.C, w.window, w.T_per, s)
+    assert_attn_close(got, ref, max_abs=1e-5, rel_l2=1e-5, what="fp32")
+
+
+def test_tiny_fp32_dense_and_full_mask():
+    torch = _torch()
+    w = synth.WORKLOADS["tiny"]
+    q, k, v = synth.iid_qkv(w.seed, w.heads, w.N, w.d)
+    note("tiny fp32 dense")
+    od = to_host(_lib.dense_attn_fwd(to_dev(q), to_dev(k), to_dev(v)))
+    ref = oracle.dense_attention(q, k, v)
+    assert_attn_close(od, ref, max_abs=1e-5, rel_l2=1e-5, what="dense fp32")
+    idx = torch.arange(w.T, dtype=torch.int32).repeat(w.T, 1).cuda()
+    cnt = torch.full((w.T,), w.T, dtype=torch.int32).cuda()
+    of = to_host(_lib.block_sparse_attn_fwd(to_dev(q), to_dev(k), to_dev(v), w.P, w.P, idx, cnt))
+    assert_attn_close(of, ref, max_abs=1e-5, rel_l2=1e-5, what="full mask fp32")
+
+
+def _bf16_inputs(seed, heads, T, H, W, d):
+    return synth.video_qkv(seed, heads, T, H, W, d)
+
+
+SMALL_LVSA = [
+    # T, H, W, heads, d, C, window, T_per   (P = H*W: multiples of 64 and ragged)
+    (6, 8, 8, 2, 128, 3, 2, 2),
+    (5, 10, 10, 2, 128, 3, 2, 3),
+    (7, 6, 26, 3, 64, 4, 3, 2),
+    (9, 5, 4, 2, 128, 4, 3, 4),     # P = 20 < 64: blocks smaller than a tile
+    (4, 3, 3, 1, 64, 2, 1, 2),      # P = 9
+    (12, 30, 52, 2, 128, 5, 3, 4),  # Wan frame size, short video
+]
+
+
+@pytest.mark.parametrize("T,H,W,heads,d,C,win,T_per", SMALL_LVSA)
+def test_bf16_lvsa_small_all_rows(T, H, W, heads, d, C, win, T_per):
+    q, k, v = _bf16_inputs(7, heads, T, H, W, d)
+    for s in range(min(T_per, 3)):
+        got, ref = _lvsa_case(q, k, v, T, H * W, C, win, T_per, s)
+        assert_attn_close(got, ref, what=f"s={s}")
+
+
+@pytest.mark.parametrize("n,heads,d", [(256, 2, 128), (1000, 2, 128), (333, 3, 64), (64, 1, 128), (1, 1, 128), (130, 2, 64)])
+def test_bf16_dense_all_rows(n, heads, d):
+    rng = np.random.default_rng(n)
+    q, k, v = (synth.bf16_round(rng.standard_normal((heads, n, d)).astype(np.float32) * sc) for sc in (2.0, 2.0, 1.0))
+    note(f"dense bf16 n={n} heads={heads} d={d}")
+    got = to_host(_lib.dense_attn_fwd(to_dev(q), to_dev(k), to_dev(v)))
+    assert_attn_close(got, oracle.dense_attention(q, k, v), what="dense")
+
+
+def test_bf16_block_list_edge_cases():
+    """Empty lists, out-of-range and negative entries, kv_cnt above max_kv,
+    a last block shorter than block_k, and a non-default scale."""
+    torch = _torch()
+    rng = np.random.default_rng(11)
+    heads, n, d, bq, bk = 2, 700, 128, 128, 96
+    q, k, v = (synth.bf16_round(rng.standard_normal((heads, n, d)).astype(np.float32)) for _ in range(3))
+    nqb, nkb = math.ceil(n / bq), math.ceil(n / bk)
+    max_kv = 5
+    idx = rng.integers(0, nkb, size=(heads, nqb, max_kv)).astype(np.int32)
+    cnt = rng.integers(0, max_kv + 1, size=(heads, nqb)).astype(np.int32)
+    idx[0, 0, :] = [7, -1, 1000, 2, 7]  # 7 is the short last block; -1 and 1000 are skipped
+    cnt[0, 0] = 5
+    cnt[1, 1] = 0  # empty key set -> zeros
+    cnt[1, 2] = 99  # clamped to max_kv
+    scale = 0.05
+    note("block list edge cases")
+    o = to_host(_lib.block_sparse_attn_fwd(to_dev(q), to_dev(k), to_dev(v), bq, bk, torch.from_numpy(idx).cuda(),
+                                           torch.from_numpy(cnt).cuda(), mask_heads=heads, scale=scale))
+    idx_o = idx.copy()
+    cnt_o = np.minimum(cnt, max_kv)
+    # the oracle takes lists of valid entries only
+    clean = np.full_like(idx_o, 0)
+    ccnt = np.zeros_like(cnt_o)
+    for h in range(heads):
+        for b in range(nqb):
+            keep = [x for x in idx_o[h, b, : cnt_o[h, b]] if 0 <= x < nkb]
+            clean[h, b, : len(keep)] = keep
+            ccnt[h, b] = len(keep)
+    ref = oracle.block_sparse_attention(q, k, v, bq, bk, clean, ccnt, mask_heads=heads, scale=scale)
+    assert_attn_close(o, ref, what="edge")
+    assert np.all(o[1, bq : 2 * bq] == 0)
+
+
+def test_bf16_closed_forms():
+    torch = _torch()
+    rng = np.random.default_rng(12)
+    heads, n, d = 2, 500, 128
+    q = synth.bf16_round(rng.standard_normal((heads, n, d)).astype(np.float32) * 3)
+    k = synth.bf16_round(rng.standard_normal((heads, n, d)).astype(np.float32) * 3)
+    row = synth.bf16_round(rng.standard_normal(d).astype(np.float32))
+    vconst = np.tile(row, (heads, n, 1))
+    note("constant V")
+    o = to_host(_lib.dense_attn_fwd(to_dev(q), to_dev(k), to_dev(vconst)))
+    assert np.abs(o - synth.bf16_to_f32(row)[None, None, :]).max() <= 1e-5  # convex combination of one row
+    v = synth.bf16_round(rng.standard_normal((heads, n, d)).astype(np.float32))
+    note("Q = 0")
+    o0 = to_host(_lib.dense_attn_fwd(to_dev(np.zeros_like(q)), to_dev(k), to_dev(v)))
+    mean = synth.bf16_to_f32(v).astype(np.float64).mean(axis=1, keepdims=True)
+    assert np.abs(o0 - mean).max() <= 1e-5
+    # one visited valid key: block_valid = 1 for that block
+    bv = np.full(math.ceil(n / 100), 100, dtype=np.int32)
+    bv[-1] = n - 100 * (len(bv) - 1)
+    bv[2] = 1
+    idx = np.full((1, len(bv), 1), 2, dtype=np.int32)
+    cnt = np.ones((1, len(bv)), dtype=np.int32)
+    note("single key")
+    o1 = to_host(_lib.block_sparse_attn_fwd(to_dev(q), to_dev(k), to_dev(v), 100, 100, torch.from_numpy(idx).cuda(),
+                                            torch.from_numpy(cnt).cuda(), block_valid=torch.from_numpy(bv).cuda()))
+    vv = synth.bf16_to_f32(v)
+    for b in range(len(bv)):
+        lo = b * 100
+        live = o1[:, lo : lo + bv[b]]
+        assert np.abs(live - vv[:, 200:201]).max() <= 1e-6
+        assert np.all(o1[:, lo + bv[b] : lo + 100] == 0)  # pad query rows
+
+
+def test_bf16_deterministic():
+    torch = _torch()
+    q, k, v = _bf16_inputs(3, 2, 6, 30, 52, 128)
+    idx, cnt = _lib.lvsa_mask(6, 3, 2, 2, 1)
+    dq, dk, dv = to_dev(q), to_dev(k), to_dev(v)
+    note("determinism")
+    outs = [to_host(_lib.block_sparse_attn_fwd(dq, dk, dv, 1560, 1560, idx, cnt)) for _ in range(3)]
+    assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
+    assert np.array_equal(outs[0].view(np.uint32), outs[2].view(np.uint32))
+
+
+def _draft_pipeline(q, k, v, T, H, W, ph, pw, sp):
+    torch = _torch()
+    heads = q.shape[0]
+    dq, dk, dv = to_dev(q), to_dev(k), to_dev(v)
+    out = _lib.draft_mask_and_perm(dq, dk, dv, T, H, W, ph, pw, sp)
+    bs = ph * pw
+    op = _lib.block_sparse_attn_fwd(out["q_perm"], out["k_perm"], out["v_perm"], bs, bs, out["kv_idx"], out["kv_cnt"],
+                                    mask_heads=heads, block_valid=out["block_valid"])
+    o = _lib.token_permute(op, out["inv_perm"])
+    torch.cuda.synchronize()
+    return out, op, o
+
+
+@pytest.mark.parametrize("T,H,W,ph,pw,heads,d,sp", [
+    (2, 10, 20, 4, 8, 2, 128, 0.6),    # block 32 < tile: small-block path
+    (3, 45, 80, 8, 16, 2, 128, 0.9),   # HunyuanVideo frame and pool, 3 frames
+    (2, 13, 21, 8, 16, 2, 64, 0.5),    # ragged tiles both ways
+    (2, 9, 30, 4, 8, 2, 128, 0.0),     # k = nb: equals dense
+])
+def test_draft_attention_small_all_rows(T, H, W, ph, pw, heads, d, sp):
+    q, k, v = _bf16_inputs(17, heads, T, H, W, d)
+    note(f"draft pipeline T={T} H={H} W={W} pool={ph}x{pw} heads={heads} d={d} sp={sp}")
+    out, op, o = _draft_pipeline(q, k, v, T, H, W, ph, pw, sp)
+    g = oracle.draft_grid(T, H, W, ph, pw)
+    kv, cnt, *_ = oracle.draft_mask(synth.bf16_to_f32(q), synth.bf16_to_f32(k), g, sp)
+    perm, inv, bv = oracle.draft_permutation(g)
+    ref = oracle.draft_attention_original_order(q, k, v, perm, inv, bv, g.block_size, kv, cnt)
+    assert_attn_close(to_host(o), ref, what="draft")
+    opn = to_host(op)
+    assert np.all(opn[:, perm < 0] == 0)  # pad rows of the reordered output
+    if sp == 0.0:
+        assert_attn_close(to_host(o), oracle.dense_attention(q, k, v), what="draft k=nb vs dense")
+
+
+# ---------------------------------------------------------------------------
+# Full-size workloads, sampled rows.
+# ---------------------------------------------------------------------------
+def _full_inputs(name):
+    w = synth.WORKLOADS[name]
+    q, k, v = synth.video_qkv(w.seed, w.heads, w.T, w.H, w.W, w.d)
+    return w, q, k, v
+
+
+def test_full_wan13b_1x_lvsa_full_mask_and_dense():
+    torch = _torch()
+    w, q, k, v = _full_inputs("wan1.3b-1x")
+    rng = np.random.default_rng(100)
+    rows = sample_frame_rows(rng, w.T, w.P, nframes=5, per_frame=96)
+    dq, dk, dv = to_dev(q), to_dev(k), to_dev(v)
+    note("wan1.3b-1x lvsa (full mask)")
+    idx, cnt = _lib.lvsa_mask(w.T, w.C, w.window, w.T_per, 0)
+    assert np.all(to_host(cnt) == w.T)
+    o = to_host(_lib.block_sparse_attn_fwd(dq, dk, dv, w.P, w.P, idx, cnt))[:, rows]
+    ref = oracle.dense_attention(q, k, v, rows=rows)
+    assert_attn_close(o, ref, what="wan1.3b-1x lvsa")
+    note("wan1.3b-1x dense")
+    od = to_host(_lib.dense_attn_fwd(dq, dk, dv))[:, rows]
+    assert_attn_close(od, ref, what="wan1.3b-1x dense")
+    del dq, dk, dv
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("s", range(8))
+def test_full_wan13b_6x_lvsa(s):
+    w, q, k, v = _cached_full("wan1.3b-6x")
+    rng = np.random.default_rng(200 + s)
+    rows = sample_frame_rows(rng, w.T, w.P, nframes=6 if s == 0 else 4, per_frame=64)
+    got, ref = _lvsa_case(q, k, v, w.T, w.P, w.C, w.window, w.T_per, s, rows=rows)
+    assert_attn_close(got, ref, what=f"wan1.3b-6x s={s}")
+
+
+def test_full_hunyuan_draft():
+    torch = _torch()
+    w, q, k, v = _full_inputs("hunyuan-draft")
+    note("hunyuan draft full pipeline")
+    out, op, o = _draft_pipeline(q, k, v, w.T, w.H, w.W, w.pool_h, w.pool_w, w.sparsity)
+    g = oracle.draft_grid(w.T, w.H, w.W, w.pool_h, w.pool_w)
+    perm, inv, bv = oracle.draft_permutation(g)
+    kv = to_host(out["kv_idx"])  # bit-exact vs the oracle: test_gpu_masks
+    cnt = to_host(out["kv_cnt"])
+    rng = np.random.default_rng(300)
+    rows = sample_frame_rows(rng, w.T, w.P, nframes=5, per_frame=64)
+    heads = [0, 7, 23]
+    ref = oracle.draft_attention_original_order(q, k, v, perm, inv, bv, g.block_size, kv, cnt, heads=heads, rows=rows)
+    got = to_host(o)[heads][:, rows]
+    assert_attn_close(got, ref, what="hunyuan draft")
+    del out, op, o
+    torch.cuda.empty_cache()
+
+
+def test_full_wan14b_6x_lvsa_and_dense():
+    torch = _torch()
+    w, q, k, v = _full_inputs("wan14b-6x")
+    rng = np.random.default_rng(400)
+    rows = sample_frame_rows(rng, w.T, w.P, nframes=4, per_frame=48)
+    heads = [0, 13, 39]
+    dq, dk, dv = to_dev(q), to_dev(k), to_dev(v)
+    note("wan14b-6x lvsa s=0")
+    idx, cnt = _lib.lvsa_mask(w.T, w.C, w.window, w.T_per, 0)
+    o = _lib.block_sparse_attn_fwd(dq, dk, dv, w.P, w.P, idx, cnt)
+    got = to_host(o[heads])[:, rows]
+    want_idx, want_cnt = oracle.lvsa_mask(w.T, w.C, w.window, w.T_per, 0)
+    ref = oracle.block_sparse_attention(q, k, v, w.P, w.P, want_idx, want_cnt, rows=rows, heads=heads)
+    assert_attn_close(got, ref, what="wan14b-6x lvsa")
+    note("wan14b-6x dense")
+    od = _lib.dense_attn_fwd(dq, dk, dv, out=o)
+    rows_d = rows[::4]
+    gd = to_host(od[heads])[:, rows_d]
+    refd = oracle.dense_attention(q, k, v, rows=rows_d, heads=heads)
+    assert_attn_close(gd, refd, what="wan14b-6x dense")
+    del dq, dk, dv, o, od
+    torch.cuda.empty_cache()
+
+
+_CACHE = {}
+
+
+def _cached_full(name):
+    if name not in _CACHE:
+        _CACHE.clear()
+        _CACHE[name] = _full_inputs(name)
+    return _CACHE[name]

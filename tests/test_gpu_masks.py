@@ -1,0 +1,132 @@
+"""GPU parity of the mask builders and the reorder, bit for bit against the oracle."""
+import numpy as np
+import pytest
+
+import oracle
+from video_diffusion_transformer_lvsa_amd import _lib, synth
+
+from helpers import note, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+LVSA_CASES = [
+    (4, 3, 2, 2, s) for s in range(4)
+] + [
+    (126, 21, 5, 8, s) for s in range(8)
+] + [
+    (21, 21, 5, 8, 0), (21, 21, 5, 8, 5), (1, 1, 1, 1, 0), (2, 5, 1, 3, 1), (8, 3, 4, 3, 0), (6, 2, 3, 1, 0),
+    (13, 40, 2, 5, 9), (300, 21, 5, 8, 3), (257, 65, 9, 16, 11), (50, 7, 20, 4, 2),
+]
+
+
+@pytest.mark.parametrize("T,C,W,T_per,s", LVSA_CASES)
+def test_lvsa_mask_bit_exact(T, C, W, T_per, s):
+    note(f"lvsa_mask T={T} C={C} W={W} T_per={T_per} s={s}")
+    idx, cnt = _lib.lvsa_mask(T, C, W, T_per, s)
+    want_idx, want_cnt = oracle.lvsa_mask(T, C, W, T_per, s, cap=idx.shape[1])
+    assert np.array_equal(to_host(cnt), want_cnt)
+    assert np.array_equal(to_host(idx), want_idx)
+
+
+def test_lvsa_mask_extra_capacity_is_padded():
+    note("lvsa_mask cap > need")
+    idx, cnt = _lib.lvsa_mask(126, 21, 5, 8, 3, cap=25)
+    want_idx, want_cnt = oracle.lvsa_mask(126, 21, 5, 8, 3, cap=25)
+    assert np.array_equal(to_host(idx), want_idx) and np.all(to_host(idx)[:, 21:] == -1)
+
+
+DRAFT_CASES = [
+    # T, H, W, pool_h, pool_w, heads, d, sparsity, dtype
+    (1, 3, 4, 2, 2, 1, 64, 0.5, "f32"),
+    (2, 10, 20, 4, 8, 2, 128, 0.6, "bf16"),
+    (3, 45, 80, 8, 16, 2, 128, 0.9, "bf16"),
+    (2, 13, 21, 8, 16, 3, 64, 0.7, "bf16"),
+    (2, 9, 30, 4, 8, 2, 64, 0.0, "f32"),
+]
+
+
+def _inputs(T, H, W, heads, d, dtype, seed):
+    if dtype == "f32":
+        q, k, v = synth.iid_qkv(seed, heads, T * H * W, d)
+        return q, k, v, q, k
+    q, k, v = synth.video_qkv(seed, heads, T, H, W, d)
+    return q, k, v, synth.bf16_to_f32(q), synth.bf16_to_f32(k)
+
+
+def _check_draft(T, H, W, ph, pw, heads, d, sp, dtype, seed):
+    q, k, v, qf, kf = _inputs(T, H, W, heads, d, dtype, seed)
+    note(f"draft_mask_and_perm T={T} H={H} W={W} pool={ph}x{pw} heads={heads} d={d} sparsity={sp} {dtype}")
+    out = _lib.draft_mask_and_perm(to_dev(q), to_dev(k), to_dev(v), T, H, W, ph, pw, sp)
+    g = oracle.draft_grid(T, H, W, ph, pw)
+    perm, inv, bv = oracle.draft_permutation(g)
+    assert np.array_equal(to_host(out["perm"]), perm)
+    assert np.array_equal(to_host(out["inv_perm"]), inv)
+    assert np.array_equal(to_host(out["block_valid"]), bv)
+    qbar, kbar = oracle.draft_pool(qf, g), oracle.draft_pool(kf, g)
+    assert np.array_equal(to_host(out["qbar"]).view(np.uint32), qbar.view(np.uint32))
+    assert np.array_equal(to_host(out["kbar"]).view(np.uint32), kbar.view(np.uint32))
+    s = oracle.draft_scores(qbar, kbar)
+    note("draft_scores")
+    gs = _lib.draft_scores(out["qbar"], out["kbar"])
+    assert np.array_equal(to_host(gs).view(np.uint32), s.view(np.uint32))
+    kk = oracle.topk_count(sp, g.nb)
+    want = oracle.draft_topk(s, kk)
+    assert np.array_equal(to_host(out["kv_cnt"]), np.full((heads, g.nb), kk, dtype=np.int32))
+    assert np.array_equal(to_host(out["kv_idx"]), want)
+    for name, x in (("q_perm", q), ("k_perm", k), ("v_perm", v)):
+        exp = np.zeros((heads, g.N_pad, d), dtype=x.dtype)
+        live = perm >= 0
+        exp[:, live] = x[:, perm[live]]
+        assert np.array_equal(to_host(out[name]), exp), name
+
+
+@pytest.mark.parametrize("case", DRAFT_CASES)
+def test_draft_bit_exact(case):
+    _check_draft(*case, seed=21)
+
+
+def test_draft_hunyuan_full_size_bit_exact():
+    w = synth.WORKLOADS["hunyuan-draft"]
+    _check_draft(w.T, w.H, w.W, w.pool_h, w.pool_w, w.heads, w.d, w.sparsity, "bf16", seed=w.seed)
+
+
+def test_draft_ties_and_zero():
+    """Q = K = 0: every score is +0 (or -0), so every row keeps blocks 0..k-1."""
+    T, H, W, heads, d = 2, 10, 20, 2, 128
+    z = np.zeros((heads, T * H * W, d), dtype=np.uint16)
+    z[0, ::3] = 0x8000  # -0.0 in bf16
+    note("draft zeros")
+    out = _lib.draft_mask_and_perm(to_dev(z), to_dev(z), to_dev(z), T, H, W, 4, 8, 0.5)
+    k = out["info"]["k"]
+    assert np.array_equal(to_host(out["kv_idx"]), np.tile(np.arange(k, dtype=np.int32), (heads, out["info"]["nb"], 1)))
+
+
+def test_draft_mask_only_without_reorder():
+    T, H, W, heads, d = 2, 10, 20, 2, 128
+    q, k, v = synth.video_qkv(5, heads, T, H, W, d)
+    note("draft no reorder")
+    out = _lib.draft_mask_and_perm(to_dev(q), to_dev(k), to_dev(v), T, H, W, 4, 8, 0.75, reorder=False)
+    g = oracle.draft_grid(T, H, W, 4, 8)
+    kv, cnt, *_ = oracle.draft_mask(synth.bf16_to_f32(q), synth.bf16_to_f32(k), g, 0.75)
+    assert np.array_equal(to_host(out["kv_idx"]), kv)
+    assert "q_perm" not in out
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 128), ("bf16", 64), ("f32", 64)])
+def test_token_permute(dtype, d):
+    import torch
+
+    rng = np.random.default_rng(3)
+    heads, n_src, n_dst = 3, 777, 1003
+    if dtype == "bf16":
+        src = rng.integers(0, 1 << 16, size=(heads, n_src, d), dtype=np.uint16)
+    else:
+        src = rng.standard_normal((heads, n_src, d)).astype(np.float32)
+    m = rng.integers(-3, n_src + 3, size=n_dst).astype(np.int32)  # -1.., and out-of-range sources -> zero rows
+    note(f"token_permute {dtype} d={d}")
+    out = _lib.token_permute(to_dev(src), torch.from_numpy(m).cuda())
+    exp = np.zeros((heads, n_dst, d), dtype=src.dtype)
+    ok = (m >= 0) & (m < n_src)
+    exp[:, ok] = src[:, m[ok]]
+    assert np.array_equal(to_host(out), exp)

@@ -1,0 +1,233 @@
+"""ctypes binding of liblvsa.so (the C ABI in include/lvsa.h).
+
+Argument marshalling only: every step of the path runs in the HIP library.
+torch is used for device memory and the current stream. The functions carry
+the ABI's names and take torch tensors; outputs are allocated with torch when
+not given. There is no fallback: if the library is missing, loading raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import re
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "liblvsa.so")
+HEADER = os.path.join(os.path.dirname(PKG), "include", "lvsa.h")
+
+LVSA_OK, LVSA_EINVAL, LVSA_ERANGE, LVSA_EDEVICE, LVSA_ENOMEM, LVSA_EUNSUPPORTED = 0, -1, -2, -3, -4, -5
+LVSA_F32, LVSA_BF16 = 0, 1
+
+_c_int, _c_sz, _c_dbl, _c_flt, _p = ctypes.c_int, ctypes.c_size_t, ctypes.c_double, ctypes.c_float, ctypes.c_void_p
+_pint = ctypes.POINTER(ctypes.c_int)
+
+SIGNATURES = {
+    "lvsa_last_error": (ctypes.c_char_p, []),
+    "lvsa_version": (ctypes.c_char_p, []),
+    "lvsa_mask_capacity": (_c_int, [_c_int] * 5),
+    "lvsa_mask": (_c_int, [_c_int] * 5 + [_p, _p, _c_int, _p]),
+    "draft_grid_info": (_c_int, [_c_int] * 5 + [_c_dbl, _pint, _pint, _pint, _pint]),
+    "draft_workspace_bytes": (_c_sz, [_c_int] * 7),
+    "draft_mask_and_perm": (_c_int, [_p, _p, _p] + [_c_int] * 8 + [_c_dbl] + [_p] * 9 + [_c_sz, _p]),
+    "draft_scores": (_c_int, [_p, _p] + [_c_int] * 4 + [_p, _p]),
+    "token_permute": (_c_int, [_p, _p] + [_c_int] * 5 + [_p, _p]),
+    "block_sparse_attn_fwd": (_c_int, [_p] * 4 + [_c_int] * 6 + [_p, _p, _c_int, _c_int, _p, _c_flt, _p]),
+    "dense_attn_fwd": (_c_int, [_p] * 4 + [_c_int] * 4 + [_c_flt, _p]),
+}
+
+_lib = None
+
+
+class LvsaError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"lvsa error {code}: {msg}")
+        self.code = code
+
+
+def load() -> ctypes.CDLL:
+    """Load liblvsa.so (built in-tree by build.py). Raises if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with `python -m video_diffusion_transformer_lvsa_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            f = getattr(lib, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def header_functions() -> list[str]:
+    """Names of the functions include/lvsa.h declares."""
+    with open(HEADER) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(\w+)\s*\(", text, flags=re.M)))
+
+
+def last_error() -> str:
+    return load().lvsa_last_error().decode()
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise LvsaError(rc, last_error())
+    return rc
+
+
+# --------------------------------------------------------------------------
+# torch-facing wrappers
+# --------------------------------------------------------------------------
+def _torch():
+    import torch
+
+    return torch
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dt(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return LVSA_BF16
+    if t.dtype == torch.float32:
+        return LVSA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _contig_cuda(*ts):
+    for t in ts:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("tensors must be contiguous CUDA (HIP) tensors")
+
+
+def lvsa_mask_capacity(T: int, C: int, window: int, T_per: int, step: int) -> int:
+    rc = load().lvsa_mask_capacity(T, C, window, T_per, step)
+    if rc < 0:
+        raise LvsaError(rc, last_error())
+    return rc
+
+
+def lvsa_mask(T: int, C: int, window: int, T_per: int, step: int, cap: int | None = None, kv_idx=None, kv_cnt=None,
+              device="cuda", stream=None):
+    """LVSA frame lists on the GPU: (kv_idx [T, cap] int32, kv_cnt [T] int32)."""
+    torch = _torch()
+    if cap is None:
+        cap = lvsa_mask_capacity(T, C, window, T_per, step)
+    if kv_idx is None:
+        kv_idx = torch.empty((T, cap), dtype=torch.int32, device=device)
+    if kv_cnt is None:
+        kv_cnt = torch.empty((T,), dtype=torch.int32, device=device)
+    _contig_cuda(kv_idx, kv_cnt)
+    _check(load().lvsa_mask(T, C, window, T_per, step, _ptr(kv_idx), _ptr(kv_cnt), cap, _stream(stream)))
+    return kv_idx, kv_cnt
+
+
+def draft_grid_info(T: int, H: int, grid_w: int, pool_h: int, pool_w: int, sparsity: float) -> dict:
+    nb, n_pad, bs, k = (ctypes.c_int() for _ in range(4))
+    _check(load().draft_grid_info(T, H, grid_w, pool_h, pool_w, sparsity, ctypes.byref(nb), ctypes.byref(n_pad),
+                                  ctypes.byref(bs), ctypes.byref(k)))
+    return {"nb": nb.value, "n_pad": n_pad.value, "block_size": bs.value, "k": k.value}
+
+
+def draft_workspace_bytes(heads: int, T: int, H: int, grid_w: int, d: int, pool_h: int, pool_w: int) -> int:
+    return int(load().draft_workspace_bytes(heads, T, H, grid_w, d, pool_h, pool_w))
+
+
+def draft_mask_and_perm(q, k, v, T: int, H: int, grid_w: int, pool_h: int, pool_w: int, sparsity: float,
+                        reorder: bool = True, stream=None) -> dict:
+    """Draft mask builder + reorder. q, k, v: [heads, T*H*grid_w, d] on the GPU.
+
+    Returns a dict with kv_idx, kv_cnt, perm, inv_perm, block_valid, the
+    reordered q_perm/k_perm/v_perm (if reorder) and qbar/kbar (views of the
+    workspace)."""
+    torch = _torch()
+    heads, n, d = q.shape
+    _contig_cuda(q, k, v)
+    info = draft_grid_info(T, H, grid_w, pool_h, pool_w, sparsity)
+    nb, n_pad, topk = info["nb"], info["n_pad"], info["k"]
+    dev = q.device
+    i32 = dict(dtype=torch.int32, device=dev)
+    out = {
+        "kv_idx": torch.empty((heads, nb, topk), **i32),
+        "kv_cnt": torch.empty((heads, nb), **i32),
+        "perm": torch.empty((n_pad,), **i32),
+        "inv_perm": torch.empty((n,), **i32),
+        "block_valid": torch.empty((nb,), **i32),
+        "info": info,
+    }
+    if reorder:
+        for name in ("q_perm", "k_perm", "v_perm"):
+            out[name] = torch.empty((heads, n_pad, d), dtype=q.dtype, device=dev)
+    ws_bytes = draft_workspace_bytes(heads, T, H, grid_w, d, pool_h, pool_w)
+    ws = torch.empty((ws_bytes // 4,), dtype=torch.float32, device=dev)
+    _check(load().draft_mask_and_perm(
+        _ptr(q), _ptr(k), _ptr(v), _dt(q), heads, T, H, grid_w, d, pool_h, pool_w, sparsity,
+        _ptr(out["kv_idx"]), _ptr(out["kv_cnt"]), _ptr(out["perm"]), _ptr(out["inv_perm"]), _ptr(out["block_valid"]),
+        _ptr(out.get("q_perm")), _ptr(out.get("k_perm")), _ptr(out.get("v_perm")), _ptr(ws), ws_bytes,
+        _stream(stream)))
+    out["qbar"] = ws[: heads * nb * d].view(heads, nb, d)
+    out["kbar"] = ws[heads * nb * d :].view(heads, nb, d)
+    return out
+
+
+def draft_scores(qbar, kbar, stream=None):
+    torch = _torch()
+    _contig_cuda(qbar, kbar)
+    heads, nbq, d = qbar.shape
+    nbk = kbar.shape[1]
+    s = torch.empty((heads, nbq, nbk), dtype=torch.float32, device=qbar.device)
+    _check(load().draft_scores(_ptr(qbar), _ptr(kbar), heads, nbq, nbk, d, _ptr(s), _stream(stream)))
+    return s
+
+
+def token_permute(src, dst_to_src, out=None, stream=None):
+    """out[h, i] = src[h, dst_to_src[i]] (zeros where the map is -1)."""
+    torch = _torch()
+    heads, n_src, d = src.shape
+    n_dst = dst_to_src.shape[0]
+    if out is None:
+        out = torch.empty((heads, n_dst, d), dtype=src.dtype, device=src.device)
+    _contig_cuda(src, dst_to_src, out)
+    _check(load().token_permute(_ptr(src), _ptr(out), _dt(src), heads, n_src, n_dst, d, _ptr(dst_to_src),
+                                _stream(stream)))
+    return out
+
+
+def block_sparse_attn_fwd(q, k, v, block_q: int, block_k: int, kv_idx, kv_cnt, mask_heads: int = 1, block_valid=None,
+                          scale: float | None = None, out=None, stream=None):
+    """Block-sparse attention; returns O fp32 [heads, n, d]."""
+    torch = _torch()
+    heads, n, d = q.shape
+    if out is None:
+        out = torch.empty((heads, n, d), dtype=torch.float32, device=q.device)
+    _contig_cuda(q, k, v, out, kv_idx, kv_cnt, block_valid)
+    max_kv = kv_idx.shape[-1]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    _check(load().block_sparse_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _dt(q), heads, n, d, block_q, block_k,
+                                        _ptr(kv_idx), _ptr(kv_cnt), max_kv, mask_heads, _ptr(block_valid), scale,
+                                        _stream(stream)))
+    return out
+
+
+def dense_attn_fwd(q, k, v, scale: float | None = None, out=None, stream=None):
+    """Dense attention; returns O fp32 [heads, n, d]."""
+    torch = _torch()
+    heads, n, d = q.shape
+    if out is None:
+        out = torch.empty((heads, n, d), dtype=torch.float32, device=q.device)
+    _contig_cuda(q, k, v, out)
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    _check(load().dense_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _dt(q), heads, n, d, scale, _stream(stream)))
+    return out

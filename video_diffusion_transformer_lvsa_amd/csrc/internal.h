@@ -1,0 +1,67 @@
+// Internal declarations shared by the host API (api.cpp) and the kernel
+// translation units. Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace lvsa {
+
+// Arguments of one attention launch (block-sparse or dense). Pointers are
+// device pointers; sizes were validated on the host.
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  float* o;
+  int heads;
+  int n;             // tokens per head
+  int block_q;       // query block size (rows)
+  int block_k;       // KV block size (rows)
+  int nqb;           // ceil(n / block_q)
+  int nkb;           // ceil(n / block_k)
+  int tiles_per_qb;  // ceil(block_q / BM) for the kernel's BM
+  int total_tiles;   // heads * nqb * tiles_per_qb
+  const int32_t* kv_idx;       // [mask_heads, nqb, max_kv] or NULL (dense)
+  const int32_t* kv_cnt;       // [mask_heads, nqb] or NULL (dense)
+  int max_kv;
+  int mask_heads;
+  const int32_t* block_valid;  // [nkb] or NULL
+  float scale_log2;            // softmax scale * log2(e)
+  float scale;                 // softmax scale
+  int dense;                   // 1: every query sees all n keys
+};
+
+// Query rows per workgroup of the bf16 MFMA kernel and of the fp32 kernel.
+constexpr int kBM_BF16 = 128;
+constexpr int kBM_F32 = 64;
+
+hipError_t launch_attn_bf16(const AttnArgs& a, int d, hipStream_t s);
+hipError_t launch_attn_f32(const AttnArgs& a, int d, hipStream_t s);
+
+hipError_t launch_lvsa_mask(int T, int C, int window, int T_per, int step, int32_t* kv_idx, int32_t* kv_cnt,
+                            int cap, hipStream_t s);
+
+struct DraftGeom {
+  int T, H, W;         // grid
+  int ph, pw, bs;      // pool tile and block size
+  int nbh, nbw, nb;    // blocks per column/row, total
+  int n, n_pad;        // tokens, padded tokens
+};
+
+hipError_t launch_draft_perm(const DraftGeom& g, int32_t* perm, int32_t* inv_perm, int32_t* block_valid,
+                             hipStream_t s);
+// Pools q and k (dtype 0 = f32, 1 = bf16) into qbar/kbar and, when the
+// *_perm pointers are non-NULL, writes the reordered tensors.
+hipError_t launch_draft_pool_gather(const DraftGeom& g, int heads, int d, int dt, const void* q, const void* k,
+                                    const void* v, float* qbar, float* kbar, void* q_perm, void* k_perm,
+                                    void* v_perm, hipStream_t s);
+hipError_t launch_draft_select(const float* qbar, const float* kbar, int heads, int nb, int d, int topk,
+                               int32_t* kv_idx, int32_t* kv_cnt, hipStream_t s);
+hipError_t launch_draft_scores(const float* qbar, const float* kbar, int heads, int nb_q, int nb_k, int d,
+                               float* scores, hipStream_t s);
+hipError_t launch_token_permute(const void* src, void* dst, int esize, int heads, int n_src, int n_dst, int d,
+                                const int32_t* map, hipStream_t s);
+
+}  // namespace lvsa
