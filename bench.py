@@ -111,6 +111,25 @@ def cpu_baseline_lvsa(w, q, k, v, budget_s: float):
     }
 
 
+def calibrate_copy(mib: int):
+    """Plain copy of known size: token_permute with the identity map over a
+    [1, rows, 128] bf16 tensor of `mib` MiB (reads and writes mib MiB)."""
+    import torch
+
+    from video_diffusion_transformer_lvsa_amd import _lib
+
+    rows = mib * (1 << 20) // 256
+    src = torch.ones((1, rows, 128), dtype=torch.bfloat16, device="cuda:0")
+    dst = torch.empty_like(src)
+    ident = torch.arange(rows, dtype=torch.int32, device="cuda:0")
+    for _ in range(3):
+        _lib.token_permute(src, ident, out=dst)
+    torch.cuda.synchronize()
+    log(f"copy calibration: {rows} rows x 256 B = {rows * 256} bytes read and written per launch")
+    del src, dst, ident
+    torch.cuda.empty_cache()
+
+
 def run_lvsa(args, w):
     import numpy as np
     import torch
@@ -316,6 +335,9 @@ def main(argv=None) -> int:
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--dense-steps", type=int, default=3)
+    ap.add_argument("--calib-copy-mb", type=int, default=0,
+                    help="first run a plain row copy (token_permute, identity map) over this many MiB, 3 times, "
+                         "so HBM counters can be scaled by a kernel of known traffic")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -331,6 +353,8 @@ def main(argv=None) -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
     _lib.load()
+    if args.calib_copy_mb > 0:
+        calibrate_copy(args.calib_copy_mb)
     w = synth.WORKLOADS[args.workload]
     res = run_draft(args, w) if w.kind == "draft" else run_lvsa(args, w)
     print(json.dumps(res), flush=True)

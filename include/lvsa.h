@@ -16,7 +16,8 @@
  *   - Tensors Q, K, V, O are [heads, n, d], row-major, contiguous, batch 1.
  *     Tokens are frame-major over the [t, h, w] grid: n = (t*H + y)*W + x.
  *   - d is 64 or 128. dtype LVSA_BF16 (bfloat16 bits) or LVSA_F32.
- *     O is always fp32.
+ *     O is always fp32. For attention, n*d must be below 2^30 (one head of
+ *     bf16 K or V stays under 2 GiB).
  *   - Every pointer argument is a device pointer (memory the caller
  *     allocated with hipMalloc or a framework allocator) unless marked
  *     "host". Device pointers must be 16-byte aligned. The caller owns every

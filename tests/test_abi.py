@@ -95,7 +95,7 @@ def test_attention_validation(lib):
     assert call(cnt=None) == _lib.LVSA_EINVAL
     assert call(bv=FAKE, bk=32) == _lib.LVSA_EINVAL
     assert call(scale=float("inf")) == _lib.LVSA_EINVAL
-    assert call(n=1 << 25) == _lib.LVSA_EINVAL  # n*d >= 2^31
+    assert call(n=1 << 23) == _lib.LVSA_EINVAL  # n*d >= 2^30
     # empty problems are valid no-ops
     assert call(heads=0) == 0
     assert call(n=0) == 0

@@ -46,12 +46,14 @@ class LvsaError(RuntimeError):
 
 
 def load() -> ctypes.CDLL:
-    """Load liblvsa.so (built in-tree by build.py). Raises if it is missing."""
+    """Load liblvsa.so (built in-tree by build.py; LVSA_LIBRARY may name another
+    build of the same library). Raises if it is missing."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise ImportError(f"{LIB_PATH} is missing: build it with `python -m video_diffusion_transformer_lvsa_amd.build`")
-        lib = ctypes.CDLL(LIB_PATH)
+        path = os.environ.get("LVSA_LIBRARY", LIB_PATH)
+        if not os.path.exists(path):
+            raise ImportError(f"{path} is missing: build it with `python -m video_diffusion_transformer_lvsa_amd.build`")
+        lib = ctypes.CDLL(path)
         for name, (res, args) in SIGNATURES.items():
             f = getattr(lib, name)
             f.restype = res

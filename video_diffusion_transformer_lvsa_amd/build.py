@@ -49,8 +49,8 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build liblvsa.so)")
 
 
-def _compile(src: str, extra: list[str]) -> str:
-    obj = os.path.join(OUT_DIR, src + ".o")
+def _compile(src: str, extra: list[str], out_dir: str = OUT_DIR) -> str:
+    obj = os.path.join(out_dir, src + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
     cmd = [hipcc(), *COMMON, *extra, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -59,26 +59,31 @@ def _compile(src: str, extra: list[str]) -> str:
     return obj
 
 
-def build(jobs: int = 5, verbose: bool = False) -> str:
-    os.makedirs(OUT_DIR, exist_ok=True)
+def build(jobs: int = 5, verbose: bool = False, lib: str = LIB, defines: tuple = ()) -> str:
+    """Compile every source and link `lib`; `defines` are extra -D flags."""
+    out_dir = OUT_DIR if lib == LIB else os.path.join(os.path.dirname(os.path.abspath(lib)), "_build")
+    os.makedirs(out_dir, exist_ok=True)
+    extra_d = [f"-D{d}" for d in defines]
     with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
-        objs = list(ex.map(lambda kv: _compile(*kv), SOURCES.items()))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda kv: _compile(kv[0], kv[1] + extra_d, out_dir), SOURCES.items()))
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {lib}")
+    return lib
 
 
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--jobs", type=int, default=5)
+    ap.add_argument("--out", default=LIB, help="library path (default: in-tree liblvsa.so)")
+    ap.add_argument("-D", dest="defines", action="append", default=[], help="extra preprocessor define")
     args = ap.parse_args(argv)
-    build(args.jobs, verbose=True)
+    build(args.jobs, verbose=True, lib=os.path.abspath(args.out), defines=tuple(args.defines))
     return 0
 
 

@@ -4,7 +4,7 @@
 // Every entry point validates its arguments before touching the GPU and
 // returns a negative lvsa_status with a thread-local message on failure; no
 // C++ exception leaves this file.
-#include "../../include/lvsa.h"
+#include "lvsa.h"
 
 #include <hip/hip_runtime.h>
 
@@ -136,7 +136,7 @@ int check_attn(const void* q, const void* k, const void* v, const float* o, int 
   if (dt != LVSA_F32 && dt != LVSA_BF16) return fail(LVSA_EINVAL, "dtype %d unknown", dt);
   if (d != 64 && d != 128) return fail(LVSA_EUNSUPPORTED, "head dim d=%d (supported: 64, 128)", d);
   if (heads < 0 || n < 0) return fail(LVSA_EINVAL, "heads=%d n=%d must be >= 0", heads, n);
-  if ((long long)n * d >= (1ll << 31)) return fail(LVSA_EINVAL, "n*d=%lld exceeds 2^31", (long long)n * d);
+  if ((long long)n * d >= (1ll << 30)) return fail(LVSA_EINVAL, "n*d=%lld exceeds 2^30", (long long)n * d);
   if (heads > 0 && n > 0) {
     if (!q || !k || !v || !o) return fail(LVSA_EINVAL, "q, k, v, o must be non-NULL");
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))

@@ -10,24 +10,28 @@
 // Design (one workgroup = 4 waves = 128 query rows; one wave = 32 rows):
 //  * The KV list of a query block is walked as one "virtual" key sequence:
 //    list slot i covers virtual rows [i*block_k, (i+1)*block_k). Tiles of
-//    BN virtual rows are gathered row by row into LDS, so a frame list of
-//    21 frames of 1560 tokens is 512 tiles of 64 with only the last one
-//    ragged, whatever the frame size.
+//    BN virtual rows are gathered row by row, so a frame list of 21 frames
+//    of 1560 tokens is 512 tiles of 64 with only the last one ragged,
+//    whatever the frame size. Rows are fetched with buffer loads; a row
+//    that is not a valid key gets an offset past the end of the buffer and
+//    reads as zero.
 //  * Scores are formed transposed, Sᵀ = K Qᵀ, with v_mfma_f32_32x32x16_bf16:
-//    the accumulator layout then gives each lane one query column and 16
-//    keys per 32x32 block, so the row max/sum of the online softmax is
-//    in-lane work plus one exchange between the two half-waves, and Pᵀ is
+//    the accumulator layout gives each lane one query column and 16 keys
+//    per 32x32 block, so the row max/sum of the online softmax is in-lane
+//    work plus one v_permlane32_swap between the half-waves, and Pᵀ is
 //    already in the B-operand layout of the second product Oᵀ += Vᵀ Pᵀ.
 //  * Q stays in VGPRs for the whole key walk. K is staged row-major in LDS,
-//    V is staged transposed (Vᵀ, keys contiguous) by an in-register 4x8
-//    transpose at staging time; both use XOR swizzles instead of padding.
-//    LDS is double-buffered: the global loads of tile i+1 are in flight
-//    while tile i is computed, one barrier per tile.
-//  * Probabilities are exp2(s*scale*log2e - m*scale*log2e), rounded to bf16
+//    V transposed (Vᵀ, keys contiguous) by an in-register 4x8 transpose;
+//    both use XOR swizzles instead of padding.
+//  * Software pipeline, one barrier per tile: while the softmax of tile i
+//    runs on the VALU, the MFMAs of Sᵀ for tile i+1 run on the matrix core
+//    (K runs one tile ahead of V in LDS, two tiles ahead in global loads).
+//  * Probabilities are exp2(s*c - m*c), c = scale*log2(e), rounded to bf16
 //    for the PV product; the row sum accumulates the same rounded values
 //    (v_dot2_f32_bf16 against ones), so O is a convex combination of V rows
-//    up to fp32 accumulation. The O rescale is skipped when no lane's max
-//    moved.
+//    up to fp32 accumulation. The reference max m is only moved when the
+//    tile max exceeds it by more than 8 (in log2 units), so O is rarely
+//    rescaled; probabilities stay <= 2^8, far inside bf16 and fp32 range.
 //  * Workgroup ids are remapped so that consecutive query tiles (same head,
 //    same query block, same key list) land on the same XCD and share its L2.
 #include "internal.h"
@@ -43,14 +47,18 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;
 constexpr int kBM = kBM_BF16;
+constexpr unsigned kInvalid = 0x80000000u;  // byte offset past every buffer: loads return 0
+constexpr float kRescale = 8.0f;            // log2 headroom before the reference max moves
+
+enum { MODE_DENSE = 0, MODE_LIST = 1, MODE_SMALL = 2 };
 
 // Where the BN virtual key rows of one tile live. Uniform across the workgroup.
-struct Tile {
-  int vt0;         // first virtual row
-  int off0;        // offset of vt0 inside its list slot
-  int blk0, blk1;  // KV block of that slot and of the next slot (-1: none)
-  int lim0, lim1;  // valid rows of those blocks
-  int full;        // all BN rows are valid keys
+// Row r < bnd is physical row base0 + r, row r >= bnd is base1 + r; row r is
+// a valid key iff r < rmax and (r < v0 or bnd <= r < v1).
+struct TileD {
+  int vt0;
+  int base0, base1, bnd, v0, v1, rmax;
+  int full;
 };
 
 __device__ __forceinline__ int block_lim(const AttnArgs& a, int b) {
@@ -65,63 +73,108 @@ __device__ __forceinline__ int block_lim(const AttnArgs& a, int b) {
 }
 
 __device__ __forceinline__ int list_entry(const AttnArgs& a, const int32_t* list, int cnt, int slot) {
-  if (slot >= cnt) return -1;
+  if (slot < 0 || slot >= cnt) return -1;
   int b = list[slot];
   return (b < 0 || b >= a.nkb) ? -1 : b;
 }
 
-template <int BN>
-__device__ __forceinline__ Tile make_tile(const AttnArgs& a, const int32_t* list, int cnt, int L, int it) {
-  Tile t;
-  t.vt0 = it * BN;
-  t.off0 = 0;
-  t.blk0 = t.blk1 = -1;
-  t.lim0 = t.lim1 = 0;
-  if (a.dense) {
-    t.full = t.vt0 + BN <= L;
-    return t;
+// Walks the tiles of one key list in order. Advancing by one tile costs a
+// few scalar operations; only positioning at a start tile divides.
+struct TileStream {
+  int vt0;          // first virtual row of the current tile
+  int slot, off;    // list slot of vt0 and the offset inside it
+  int blk0, lim0;   // KV block of that slot and its valid rows
+  int blk1, lim1;   // the same for the next slot
+};
+
+template <int BN, int MODE>
+__device__ __forceinline__ void stream_init(TileStream& ts, const AttnArgs& a, const int32_t* list, int cnt, int it) {
+  ts.vt0 = it * BN;
+  ts.slot = ts.off = 0;
+  ts.blk0 = ts.blk1 = -1;
+  ts.lim0 = ts.lim1 = 0;
+  if (MODE == MODE_LIST) {
+    ts.slot = ts.vt0 / a.block_k;
+    ts.off = ts.vt0 - ts.slot * a.block_k;
+    ts.blk0 = list_entry(a, list, cnt, ts.slot);
+    ts.lim0 = block_lim(a, ts.blk0);
+    ts.blk1 = list_entry(a, list, cnt, ts.slot + 1);
+    ts.lim1 = block_lim(a, ts.blk1);
   }
-  if (a.block_k >= BN) {
-    int slot = t.vt0 / a.block_k;
-    t.off0 = t.vt0 - slot * a.block_k;
-    t.blk0 = list_entry(a, list, cnt, slot);
-    t.blk1 = list_entry(a, list, cnt, slot + 1);
-    t.lim0 = block_lim(a, t.blk0);
-    t.lim1 = block_lim(a, t.blk1);
-    bool in_len = t.vt0 + BN <= L;
-    if (t.off0 + BN <= a.block_k)
-      t.full = in_len && (t.off0 + BN <= t.lim0);
-    else
-      t.full = in_len && (t.lim0 == a.block_k) && (t.off0 + BN - a.block_k <= t.lim1);
+}
+
+template <int BN, int MODE>
+__device__ __forceinline__ void stream_next(TileStream& ts, const AttnArgs& a, const int32_t* list, int cnt) {
+  ts.vt0 += BN;
+  if (MODE == MODE_LIST) {
+    ts.off += BN;
+    if (ts.off >= a.block_k) {  // block_k >= BN: at most one slot per tile
+      ts.off -= a.block_k;
+      ts.slot += 1;
+      ts.blk0 = ts.blk1;
+      ts.lim0 = ts.lim1;
+      ts.blk1 = list_entry(a, list, cnt, ts.slot + 1);
+      ts.lim1 = block_lim(a, ts.blk1);
+    }
+  }
+}
+
+template <int BN, int MODE>
+__device__ __forceinline__ TileD stream_tile(const TileStream& ts, const AttnArgs& a, int L) {
+  TileD t;
+  t.vt0 = ts.vt0;
+  t.rmax = L - ts.vt0;
+  if (MODE == MODE_DENSE) {
+    t.base0 = t.base1 = ts.vt0;
+    t.bnd = BN;
+    t.v0 = t.rmax;
+    t.v1 = 0;
+    t.full = t.rmax >= BN;
+  } else if (MODE == MODE_LIST) {
+    t.bnd = a.block_k - ts.off;
+    t.base0 = ts.blk0 * a.block_k + ts.off;
+    t.base1 = ts.blk1 * a.block_k - t.bnd;
+    t.v0 = min(t.bnd, ts.lim0 - ts.off);
+    t.v1 = t.bnd + ts.lim1;
+    t.full = t.rmax >= BN && t.v0 >= min(t.bnd, BN) && (t.bnd >= BN || t.v1 >= BN);
   } else {
+    t.base0 = t.base1 = t.bnd = t.v0 = t.v1 = 0;
     t.full = 0;
   }
   return t;
 }
 
-// Physical row (within the head) of virtual row vt0 + r, or -1 if that key is invalid.
-template <int BN>
-__device__ __forceinline__ int row_phys(const AttnArgs& a, const Tile& t, const int32_t* list, int cnt, int L, int r) {
-  int vj = t.vt0 + r;
-  if (vj >= L) return -1;
-  if (a.dense) return vj;
-  if (a.block_k >= BN) {
-    int pos = t.off0 + r;
-    bool second = pos >= a.block_k;
-    int blk = second ? t.blk1 : t.blk0;
-    int off = second ? pos - a.block_k : pos;
-    int lim = second ? t.lim1 : t.lim0;
-    return off < lim ? blk * a.block_k + off : -1;
+// Physical row of tile row r, or -1 if r is not a valid key.
+template <int BN, int MODE>
+__device__ __forceinline__ int tile_row(const AttnArgs& a, const TileD& t, const int32_t* list, int cnt, int r) {
+  if (MODE == MODE_SMALL) {
+    const int vj = t.vt0 + r;
+    if (r >= t.rmax) return -1;
+    const int slot = vj / a.block_k;
+    const int off = vj - slot * a.block_k;
+    const int blk = list_entry(a, list, cnt, slot);
+    return off < block_lim(a, blk) ? blk * a.block_k + off : -1;
   }
-  int slot = vj / a.block_k;
-  int off = vj - slot * a.block_k;
-  int blk = list_entry(a, list, cnt, slot);
-  return off < block_lim(a, blk) ? blk * a.block_k + off : -1;
+  const bool ok = (r < t.rmax) & ((r < t.v0) | ((r >= t.bnd) & (r < t.v1)));
+  const int p = (r < t.bnd ? t.base0 : t.base1) + r;
+  return ok ? p : -1;
 }
 
-__device__ __forceinline__ float other_half(float x) { return __shfl_xor(x, 32, 64); }
+// Both half-waves end with f(x[l], x[l ^ 32]).
+__device__ __forceinline__ float half_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
-template <int D, int BN>
+__device__ __forceinline__ u32x4 bload(__amdgpu_buffer_rsrc_t r, unsigned off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+
+template <int D, int BN, int MODE>
 __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_bf16_kernel(AttnArgs a) {
   constexpr int KSTEPS = D / 16;   // k-steps of Sᵀ = K Qᵀ
   constexpr int NKB = BN / 32;     // 32-key blocks per tile
@@ -130,6 +183,7 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_bf16_kernel(AttnArgs a) {
   constexpr int CPR = D / 8;       // 16-byte chunks per K row
   constexpr int RPI = kThreads / CPR;  // K rows per load instruction
   constexpr int KJ = BN / RPI;     // K rows per thread
+  constexpr int NKGB = BN / 32;    // 8-key-group blocks of the V loader
   static_assert(KJ == 4, "tile shape");
   static_assert((BN / 4) * (D / 8) == kThreads, "one 4x8 V unit per thread");
 
@@ -164,18 +218,22 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_bf16_kernel(AttnArgs a) {
   const int qend = min(blk_lo + qlim, blk_end);
   const int row_lo = blk_lo + qt * kBM;
   const int qrow = row_lo + wave * 32 + l32;
-  const bool q_in_blk = qrow < blk_end && (qrow - blk_lo) < (qt + 1) * kBM;
+  const bool q_in_blk = qrow < blk_end;
   const bool q_valid = qrow < qend;
 
   const size_t head_off = (size_t)h * (size_t)a.n * D;
-  const uint16_t* __restrict__ Qh = (const uint16_t*)a.q + head_off;
-  const uint16_t* __restrict__ Kh = (const uint16_t*)a.k + head_off;
-  const uint16_t* __restrict__ Vh = (const uint16_t*)a.v + head_off;
+  const int head_bytes = a.n * D * 2;
+  const __amdgpu_buffer_rsrc_t Qr =
+      __builtin_amdgcn_make_buffer_rsrc((void*)((const uint16_t*)a.q + head_off), (short)0, head_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t Kr =
+      __builtin_amdgcn_make_buffer_rsrc((void*)((const uint16_t*)a.k + head_off), (short)0, head_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t Vr =
+      __builtin_amdgcn_make_buffer_rsrc((void*)((const uint16_t*)a.v + head_off), (short)0, head_bytes, 0x00020000);
   float* __restrict__ Oh = a.o + head_off;
 
   const int32_t* list = nullptr;
   int cnt = 0, L = a.n;
-  if (!a.dense) {
+  if (MODE != MODE_DENSE) {
     const int hm = a.mask_heads > 1 ? h : 0;
     const int base = hm * a.nqb + qb;
     cnt = a.kv_cnt[base];
@@ -190,62 +248,99 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_bf16_kernel(AttnArgs a) {
   bf16x8 qreg[KSTEPS];
 #pragma unroll
   for (int kk = 0; kk < KSTEPS; ++kk) {
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (q_valid) v = *(const u32x4*)(Qh + qrow * D + 16 * kk + 8 * half);
-    qreg[kk] = __builtin_bit_cast(bf16x8, v);
+    const unsigned off = q_valid ? (unsigned)((qrow * D + 16 * kk + 8 * half) * 2) : kInvalid;
+    qreg[kk] = __builtin_bit_cast(bf16x8, bload(Qr, off));
   }
 
-  // Loader roles. K: thread = (row r0 + RPI*j, 16-byte chunk kc).
+  // Loader roles. K: thread = (row kr0 + RPI*j, 16-byte chunk kc).
   const int kc = tid % CPR;
   const int kr0 = tid / CPR;
   // V: thread = 4 keys (4*vkg .. +3) x 8 channels (8*vdg .. +7); within a wave
-  // 8 key groups x 8 channel groups, arranged so LDS writes are conflict-free.
-  constexpr int NKGB = BN / 32;
+  // 8 key groups x 8 channel groups, arranged so the LDS writes are conflict-free.
   const int vkg = (lane & 7) + 8 * (wave % NKGB);
   const int vdg = 2 * (lane >> 4) + ((lane >> 3) & 1) + 8 * (wave / NKGB);
 
   u32x4 kreg[KJ], vreg[4];
-  int kphys[KJ];
+  unsigned vok = 0;
 
-  auto load_tile = [&](const Tile& t) {
+  // Per-thread byte offsets of the loader rows inside a tile whose rows are
+  // one contiguous run (the common case); the run's start is a scalar offset.
+  const unsigned kofs = (unsigned)((kr0 * D + 8 * kc) * 2);        // + j * RPI*D*2 for row j
+  const unsigned vofs = (unsigned)((4 * vkg * D + 8 * vdg) * 2);   // + j * D*2 for row j
+
+  // A tile is "simple" when all BN rows are valid keys of one block run.
+  auto simple = [&](const TileD& t) { return t.full && t.bnd >= BN; };
+
+  auto load_k = [&](const TileD& t) {
+    if (simple(t)) {
+      const unsigned so = (unsigned)(t.base0 * D * 2);
 #pragma unroll
-    for (int j = 0; j < KJ; ++j) {
-      int p = row_phys<BN>(a, t, list, cnt, L, kr0 + RPI * j);
-      kphys[j] = p;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (p >= 0) v = *(const u32x4*)(Kh + p * D + 8 * kc);
-      kreg[j] = v;
-    }
+      for (int j = 0; j < KJ; ++j)
+        kreg[j] = __builtin_amdgcn_raw_buffer_load_b128(Kr, kofs, so + (unsigned)(j * RPI * D * 2), 0);
+    } else {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      int p = row_phys<BN>(a, t, list, cnt, L, 4 * vkg + j);
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (p >= 0) v = *(const u32x4*)(Vh + p * D + 8 * vdg);
-      vreg[j] = v;
+      for (int j = 0; j < KJ; ++j) {
+        const int p = tile_row<BN, MODE>(a, t, list, cnt, kr0 + RPI * j);
+        kreg[j] = bload(Kr, p >= 0 ? (unsigned)((p * D + 8 * kc) * 2) : kInvalid);
+      }
     }
   };
-
-  auto store_tile = [&](int st) {
+  auto load_v = [&](const TileD& t) {
+    if (simple(t)) {
+      const unsigned so = (unsigned)(t.base0 * D * 2);
+      vok = 0x01010101u;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) vreg[j] = __builtin_amdgcn_raw_buffer_load_b128(Vr, vofs + j * D * 2, so, 0);
+    } else {
+      vok = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int p = tile_row<BN, MODE>(a, t, list, cnt, 4 * vkg + j);
+        vok |= (p >= 0 ? 1u : 0u) << (8 * j);
+        vreg[j] = bload(Vr, p >= 0 ? (unsigned)((p * D + 8 * vdg) * 2) : kInvalid);
+      }
+    }
+  };
+  // LDS swizzles (no padding). K: 16-byte chunk c of row r sits at chunk
+  // c ^ (r & KSW). Vᵀ: 8-byte chunk c (4 keys) of row d sits at c ^ vsw(d).
+  // Both keep 16 consecutive rows of a read (and of a write) on distinct banks
+  // for 32 and for 64 four-byte banks.
+  constexpr int KSW = CPR >= 16 ? 15 : CPR - 1;
+  auto vsw = [](int d) { return BN == 64 ? ((d & 15) ^ ((d >> 4) & 1)) : (d & 31); };
+  auto store_k = [&](int st) {
 #pragma unroll
     for (int j = 0; j < KJ; ++j) {
-      int r = kr0 + RPI * j;
-      Ks[st][r * CPR + (kc ^ (r & 7))] = kreg[j];
+      const int r = kr0 + RPI * j;
+      Ks[st][r * CPR + (kc ^ (r & KSW))] = kreg[j];
     }
-    // 4 keys x 8 channels -> 8 rows of Vᵀ, each 4 keys (8 bytes).
+  };
+  auto store_v = [&](int st) {
+    // 4 keys x 8 channels -> 8 rows of Vᵀ, each 4 keys (8 bytes): byte
+    // permutes pick the low (even channel) or high (odd channel) halves.
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      unsigned int e01 = (vreg[0][m] & 0xffffu) | (vreg[1][m] << 16);
-      unsigned int e23 = (vreg[2][m] & 0xffffu) | (vreg[3][m] << 16);
-      unsigned int o01 = (vreg[0][m] >> 16) | (vreg[1][m] & 0xffff0000u);
-      unsigned int o23 = (vreg[2][m] >> 16) | (vreg[3][m] & 0xffff0000u);
-      int d0 = 8 * vdg + 2 * m;
-      int d1 = d0 + 1;
-      Vs[st][d0 * (BN / 4) + (vkg ^ (d0 & 15))] = u32x2{e01, e23};
-      Vs[st][d1 * (BN / 4) + (vkg ^ (d1 & 15))] = u32x2{o01, o23};
+      const unsigned e01 = __builtin_amdgcn_perm(vreg[1][m], vreg[0][m], 0x05040100u);
+      const unsigned e23 = __builtin_amdgcn_perm(vreg[3][m], vreg[2][m], 0x05040100u);
+      const unsigned o01 = __builtin_amdgcn_perm(vreg[1][m], vreg[0][m], 0x07060302u);
+      const unsigned o23 = __builtin_amdgcn_perm(vreg[3][m], vreg[2][m], 0x07060302u);
+      const int d0 = 8 * vdg + 2 * m;
+      const int d1 = d0 + 1;
+      Vs[st][d0 * (BN / 4) + (vkg ^ vsw(d0))] = u32x2{e01, e23};
+      Vs[st][d1 * (BN / 4) + (vkg ^ vsw(d1))] = u32x2{o01, o23};
     }
-    if (kc == 0) {
+    if (vdg == 0) kval[st][vkg] = vok;  // validity bytes of keys 4*vkg .. +3
+  };
+  auto qk = [&](int st, f32x16 (&s)[NKB]) {
+    const f32x16 zero = {};
 #pragma unroll
-      for (int j = 0; j < KJ; ++j) ((unsigned char*)kval[st])[kr0 + RPI * j] = kphys[j] >= 0 ? 1 : 0;
+    for (int kk = 0; kk < KSTEPS; ++kk) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const int r = kb * 32 + l32;
+        const int ch = 2 * kk + half;
+        const bf16x8 A = __builtin_bit_cast(bf16x8, Ks[st][r * CPR + (ch ^ (r & KSW))]);
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, qreg[kk], kk == 0 ? zero : s[kb], 0, 0, 0);
+      }
     }
   };
 
@@ -254,76 +349,74 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_bf16_kernel(AttnArgs a) {
   for (int i = 0; i < NDB; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[i][r] = 0.f;
-  float m_run = -INFINITY;
+  float mc = -INFINITY;  // reference max, already multiplied by c
   float l_run = 0.f;
   const float c = a.scale_log2;
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  Tile cur = make_tile<BN>(a, list, cnt, L, 0);
+  f32x16 s[NKB], sn[NKB];
+  int full_cur = 1;
+  TileStream ks;  // the K stream, two tiles ahead of the tile being reduced
+  stream_init<BN, MODE>(ks, a, list, cnt, 0);
+  TileD tprev;  // descriptor of the tile whose K was loaded last (V follows one step later)
   if (ntiles > 0) {
-    load_tile(cur);
-    store_tile(0);
+    const TileD t0 = stream_tile<BN, MODE>(ks, a, L);
+    stream_next<BN, MODE>(ks, a, list, cnt);
+    const TileD t1 = stream_tile<BN, MODE>(ks, a, L);
+    stream_next<BN, MODE>(ks, a, list, cnt);
+    load_k(t0);
+    load_v(t0);
+    store_k(0);
+    store_v(0);
+    load_k(t1);
+    store_k(1);
+    full_cur = t0.full;
+    tprev = t1;
   }
   __syncthreads();
+  if (ntiles > 0) qk(0, s);
+  __syncthreads();
 
-  for (int it = 0; it < ntiles; ++it) {
+  // One pipeline step: tile `it` is in `cur` (raw scores) and `nxt` receives tile it+1.
+  auto step = [&](int it, f32x16 (&cur)[NKB], f32x16 (&nxt)[NKB]) {
     const int st = it & 1;
-    const bool more = it + 1 < ntiles;
-    Tile nxt;
-    if (more) {
-      nxt = make_tile<BN>(a, list, cnt, L, it + 1);
-      load_tile(nxt);
-    }
+    // Global loads: K two tiles ahead, V one tile ahead (past the end they read zeros).
+    const TileD tk = stream_tile<BN, MODE>(ks, a, L);
+    stream_next<BN, MODE>(ks, a, list, cnt);
+    const TileD tv = tprev;
+    tprev = tk;
+    load_k(tk);
+    load_v(tv);
 
-    // Sᵀ = K Qᵀ for this tile: NKB accumulators of 32 keys x 32 queries.
-    f32x16 s[NKB];
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-#pragma unroll
-    for (int kk = 0; kk < KSTEPS; ++kk) {
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        const int r = kb * 32 + l32;
-        const int ch = 2 * kk + half;
-        bf16x8 A = __builtin_bit_cast(bf16x8, Ks[st][r * CPR + (ch ^ (r & 7))]);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, qreg[kk], s[kb], 0, 0, 0);
-      }
-    }
-
-    // Mask invalid keys. Accumulator register r of block kb holds key
-    // kb*32 + 8*(r/4) + 4*half + r%4 of the tile.
-    if (!cur.full) {
+    // Mask the invalid keys of tile i. Accumulator register r of block kb
+    // holds key kb*32 + 8*(r/4) + 4*half + r%4 of the tile.
+    if (!full_cur) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          unsigned int f4 = kval[st][(kb * 32 + 8 * g + 4 * half) >> 2];
+          const unsigned f4 = kval[st][(kb * 32 + 8 * g + 4 * half) >> 2];
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            if (((f4 >> (8 * i)) & 0xffu) == 0u) s[kb][4 * g + i] = -INFINITY;
+            if (((f4 >> (8 * i)) & 0xffu) == 0u) cur[kb][4 * g + i] = -INFINITY;
         }
     }
+
+    // Sᵀ of tile i+1 on the matrix core while the VALU does the softmax of tile i.
+    qk(st ^ 1, nxt);
 
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = fmaxf(mx, other_half(mx));
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f((m_run - m_use) * c);
-    if (__ballot(alpha != 1.f) != 0ull) {
-      l_run *= alpha;
-#pragma unroll
-      for (int i = 0; i < NDB; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
-    }
-    m_run = m_new;
-    const float nm = -m_use * c;
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, cur[kb][r]);
+    mx = half_max(mx) * c;
+    const bool need = mx > mc + kRescale;
+    const float mc_new = need ? mx : mc;
+    const float alpha = need ? __builtin_amdgcn_exp2f(mc - mc_new) : 1.f;
+    mc = mc_new;
+    l_run *= alpha;
+    const float nm = (mc == -INFINITY) ? 0.f : -mc;
 
     // Pᵀ in the B-operand layout of Oᵀ += Vᵀ Pᵀ: step kk takes registers
     // 8*(kk%2) .. +7 of block kk/2, i.e. keys 16*kk + 8*(j/4) + 4*half + j%4.
@@ -332,13 +425,21 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_bf16_kernel(AttnArgs a) {
     for (int kk = 0; kk < PVSTEPS; ++kk) {
 #pragma unroll
       for (int j = 0; j < 8; j += 2) {
-        const float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kk >> 1][8 * (kk & 1) + j], c, nm));
-        const float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kk >> 1][8 * (kk & 1) + j + 1], c, nm));
-        bf16x2 p2 = {(__bf16)x0, (__bf16)x1};
+        const float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(cur[kk >> 1][8 * (kk & 1) + j], c, nm));
+        const float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(cur[kk >> 1][8 * (kk & 1) + j + 1], c, nm));
+        const bf16x2 p2 = {(__bf16)x0, (__bf16)x1};
         l_run = __builtin_amdgcn_fdot2_f32_bf16(p2, ones, l_run, false);
         pb[kk][j] = p2[0];
         pb[kk][j + 1] = p2[1];
       }
+    }
+    // The rescale test waits for the row sum so the branch cannot split the
+    // block above (l_run == l_run is false only for NaN).
+    if (__ballot(need && (l_run == l_run)) != 0ull) {
+#pragma unroll
+      for (int i = 0; i < NDB; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
     }
 
     // Oᵀ += Vᵀ Pᵀ. A operand: row d = 32*db + l32, keys of chunks 4*kk + half
@@ -348,25 +449,33 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_bf16_kernel(AttnArgs a) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
         const int d = db * 32 + l32;
-        const u32x2 lo = Vs[st][d * (BN / 4) + ((4 * kk + half) ^ (d & 15))];
-        const u32x2 hi = Vs[st][d * (BN / 4) + ((4 * kk + 2 + half) ^ (d & 15))];
+        const u32x2 lo = Vs[st][d * (BN / 4) + ((4 * kk + half) ^ vsw(d))];
+        const u32x2 hi = Vs[st][d * (BN / 4) + ((4 * kk + 2 + half) ^ vsw(d))];
         const u32x4 A4 = {lo[0], lo[1], hi[0], hi[1]};
         oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, A4), pb[kk], oacc[db], 0, 0, 0);
       }
     }
 
-    if (more) {
-      store_tile(st ^ 1);
-      cur = nxt;
-    }
+    // K of tile i+2 replaces K of tile i (read last iteration); V of tile i+1
+    // replaces V of tile i-1 (read last iteration).
+    store_k(st);
+    store_v(st ^ 1);
+    full_cur = tv.full;
     __syncthreads();
+  };
+
+  int it = 0;
+  for (; it + 1 < ntiles; it += 2) {
+    step(it, s, sn);
+    step(it + 1, sn, s);
   }
+  if (it < ntiles) step(it, s, sn);
 
   // Epilogue: combine the two half-waves' partial sums, normalise, store fp32.
-  const float l_tot = l_run + other_half(l_run);
+  const float l_tot = half_sum(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (q_in_blk) {
-    float* orow = Oh + qrow * D;
+    float* orow = Oh + (size_t)qrow * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -384,16 +493,23 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_bf16_kernel(AttnArgs a) {
   }
 }
 
+template <int D, int BN>
+hipError_t launch_mode(const AttnArgs& a, hipStream_t s) {
+  dim3 grid(a.total_tiles), block(kThreads);
+  if (a.dense)
+    hipLaunchKernelGGL((bsa_fwd_bf16_kernel<D, BN, MODE_DENSE>), grid, block, 0, s, a);
+  else if (a.block_k >= BN)
+    hipLaunchKernelGGL((bsa_fwd_bf16_kernel<D, BN, MODE_LIST>), grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL((bsa_fwd_bf16_kernel<D, BN, MODE_SMALL>), grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_attn_bf16(const AttnArgs& a, int d, hipStream_t s) {
   if (a.total_tiles == 0) return hipSuccess;
-  dim3 grid(a.total_tiles), block(kThreads);
-  if (d == 128)
-    hipLaunchKernelGGL((bsa_fwd_bf16_kernel<128, 64>), grid, block, 0, s, a);
-  else
-    hipLaunchKernelGGL((bsa_fwd_bf16_kernel<64, 128>), grid, block, 0, s, a);
-  return hipGetLastError();
+  return d == 128 ? launch_mode<128, 64>(a, s) : launch_mode<64, 128>(a, s);
 }
 
 }  // namespace lvsa
