@@ -61,11 +61,16 @@ struct TileD {
   int full;
 };
 
+// Index data is read through the constant address space: it is not written
+// during the kernel, and uniform reads then become scalar loads.
+typedef const __attribute__((address_space(4))) int32_t cint32;
+__device__ __forceinline__ int32_t cload(const int32_t* p, int i) { return ((cint32*)p)[i]; }
+
 __device__ __forceinline__ int block_lim(const AttnArgs& a, int b) {
   if (b < 0 || b >= a.nkb) return 0;
   int lim = a.block_k;
   if (a.block_valid) {
-    int bv = a.block_valid[b];
+    int bv = cload(a.block_valid, b);
     lim = bv < 0 ? 0 : (bv < lim ? bv : lim);
   }
   int rem = a.n - b * a.block_k;
@@ -74,7 +79,7 @@ __device__ __forceinline__ int block_lim(const AttnArgs& a, int b) {
 
 __device__ __forceinline__ int list_entry(const AttnArgs& a, const int32_t* list, int cnt, int slot) {
   if (slot < 0 || slot >= cnt) return -1;
-  int b = list[slot];
+  int b = cload(list, slot);
   return (b < 0 || b >= a.nkb) ? -1 : b;
 }
 
@@ -493,6 +498,299 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_bf16_kernel(AttnArgs a) {
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// d = 128: K and V tiles go from HBM straight into LDS (buffer loads with an
+// LDS destination, 16 bytes per lane), so no VGPRs hold staged rows and no
+// instructions write LDS; the Vᵀ operand of the PV product is read from the
+// row-major V tile with ds_read_b64_tr_b16. In a group of 16 lanes that
+// instruction gives lane j element j%4 of the 8 bytes read by lanes
+// 4m + j/4 (m = 0..3): when lane i reads keys kb + i/4, channels
+// dbase + 4*(i%4) .. +3, lane j receives channel dbase + j of keys kb..kb+3,
+// which is exactly four k-slots of the MFMA A operand.
+// LDS rows are 256 bytes (16 chunks of 16 bytes); chunk c of row r is stored
+// at c ^ (r & 15) for K and at c ^ gv(r & 3), gv = {0, 4, 10, 14}, for V:
+// both keep every read conflict-free with 32 and with 64 banks.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int gv_swz(int x) { return 4 * x + 2 * (x >> 1); }
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+
+template <int MODE>
+__global__ __launch_bounds__(kThreads, 2) void bsa_fwd_d128_kernel(AttnArgs a) {
+  constexpr int D = 128, BN = 64, KSTEPS = 8, NKB = 2, PVSTEPS = 4, NDB = 4;
+  constexpr int TILE = BN * D * 2;  // 16 KB per K or V tile
+  // Four separate LDS objects (K and V of two stages) so the compiler can see
+  // that reading one stage does not wait for the loads filling the other.
+  __shared__ __attribute__((aligned(1024))) unsigned char ks0[TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char ks1[TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char vs0[TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char vs1[TILE];
+  __shared__ unsigned int kval[2][BN / 4];
+  auto kbuf = [&](int st) -> unsigned char* { return st == 0 ? ks0 : ks1; };
+  auto vbuf = [&](int st) -> unsigned char* { return st == 0 ? vs0 : vs1; };
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = lane >> 5;
+  const int l32 = lane & 31;
+
+  const int G = a.total_tiles;
+  const int w = blockIdx.x;
+  const int xcd = w & 7, idx = w >> 3, q8 = G >> 3, r8 = G & 7;
+  const int logical = (xcd < r8 ? xcd * (q8 + 1) : r8 * (q8 + 1) + (xcd - r8) * q8) + idx;
+  const int qt = logical % a.tiles_per_qb;
+  const int rest = logical / a.tiles_per_qb;
+  const int qb = rest % a.nqb;
+  const int h = rest / a.nqb;
+
+  const int blk_lo = qb * a.block_q;
+  const int blk_end = min(blk_lo + a.block_q, a.n);
+  int qlim = a.block_q;
+  if (a.block_valid) {
+    int bv = a.block_valid[qb];
+    qlim = bv < 0 ? 0 : (bv < qlim ? bv : qlim);
+  }
+  const int qend = min(blk_lo + qlim, blk_end);
+  const int row_lo = blk_lo + qt * kBM;
+  const int qrow = row_lo + wave * 32 + l32;
+  const bool q_in_blk = qrow < blk_end;
+  const bool q_valid = qrow < qend;
+
+  const size_t head_off = (size_t)h * (size_t)a.n * D;
+  const int head_bytes = a.n * D * 2;
+  const __amdgpu_buffer_rsrc_t Qr =
+      __builtin_amdgcn_make_buffer_rsrc((void*)((const uint16_t*)a.q + head_off), (short)0, head_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t Kr =
+      __builtin_amdgcn_make_buffer_rsrc((void*)((const uint16_t*)a.k + head_off), (short)0, head_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t Vr =
+      __builtin_amdgcn_make_buffer_rsrc((void*)((const uint16_t*)a.v + head_off), (short)0, head_bytes, 0x00020000);
+  float* __restrict__ Oh = a.o + head_off;
+
+  const int32_t* list = nullptr;
+  int cnt = 0, L = a.n;
+  if (MODE != MODE_DENSE) {
+    const int hm = a.mask_heads > 1 ? h : 0;
+    const int base = hm * a.nqb + qb;
+    cnt = a.kv_cnt[base];
+    cnt = cnt < 0 ? 0 : (cnt > a.max_kv ? a.max_kv : cnt);
+    list = a.kv_idx + (size_t)base * a.max_kv;
+    L = cnt * a.block_k;
+  }
+  if (row_lo >= qend) L = 0;
+  const int ntiles = (L + BN - 1) / BN;
+
+  bf16x8 qreg[KSTEPS];
+#pragma unroll
+  for (int kk = 0; kk < KSTEPS; ++kk) {
+    const unsigned off = q_valid ? (unsigned)((qrow * D + 16 * kk + 8 * half) * 2) : kInvalid;
+    qreg[kk] = __builtin_bit_cast(bf16x8, bload(Qr, off));
+  }
+
+  // DMA roles: instruction j of wave `wave` fills tile rows 16j + 4*wave .. +3;
+  // lane writes row 16j + dR, LDS chunk dp.
+  const int dR = 4 * wave + (lane >> 4);
+  const int dp = lane & 15;
+  const unsigned kdma = (unsigned)(dR * 256 + 16 * (dp ^ (dR & 15)));
+  const unsigned vdma = (unsigned)(dR * 256 + 16 * (dp ^ gv_swz(dR & 3)));
+
+  // LDS read addresses (bytes inside a stage). K: row kb*32 + l32, chunk 2kk + half.
+  unsigned kra[KSTEPS];
+#pragma unroll
+  for (int kk = 0; kk < KSTEPS; ++kk) kra[kk] = (unsigned)(l32 * 256 + 16 * ((2 * kk + half) ^ (l32 & 15)));
+  // Vᵀ via transpose reads: lane (group g = lane/16, i = lane%16) reads keys
+  // 16kk + 8s + 4*(g/2) + i/4, channels 32db + 16*(g%2) + 4*(i%4) .. +3.
+  const int ti = lane & 15, tg = lane >> 4;
+  unsigned vra[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+    vra[db] = (unsigned)((4 * (tg >> 1) + (ti >> 2)) * 256 +
+                         16 * ((4 * db + 2 * (tg & 1) + ((ti & 3) >> 1)) ^ gv_swz(ti >> 2)) + 8 * (ti & 1));
+
+  auto simple = [&](const TileD& t) { return t.full && t.bnd >= BN; };
+  auto dma = [&](__amdgpu_buffer_rsrc_t r, int st, int kind, int j, unsigned voff, unsigned soff) {
+    unsigned char* dst = (kind == 0 ? kbuf(st) : vbuf(st)) + 4096 * j + 1024 * wave;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, voff, soff, 0, 0);
+  };
+  auto load_k = [&](const TileD& t, int st) {
+    if (simple(t)) {
+      const unsigned so = (unsigned)(t.base0 * D * 2);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dma(Kr, st, 0, j, kdma, so + 4096u * j);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int R = 16 * j + dR;
+        const int p = tile_row<BN, MODE>(a, t, list, cnt, R);
+        dma(Kr, st, 0, j, p >= 0 ? (unsigned)(p * 256 + 16 * (dp ^ (R & 15))) : kInvalid, 0u);
+      }
+    }
+  };
+  auto load_v = [&](const TileD& t, int st) {
+    if (simple(t)) {
+      const unsigned so = (unsigned)(t.base0 * D * 2);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dma(Vr, st, 1, j, vdma, so + 4096u * j);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int R = 16 * j + dR;
+        const int p = tile_row<BN, MODE>(a, t, list, cnt, R);
+        dma(Vr, st, 1, j, p >= 0 ? (unsigned)(p * 256 + 16 * (dp ^ gv_swz(R & 3))) : kInvalid, 0u);
+        if (dp == 0) ((unsigned char*)kval[st])[R] = p >= 0 ? 1 : 0;
+      }
+    }
+  };
+  auto qk = [&](int st, f32x16 (&s)[NKB]) {
+    const f32x16 zero = {};
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const bf16x8 A = __builtin_bit_cast(bf16x8, *(const u32x4*)(kbuf(st) + kb * 8192 + kra[kk]));
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, qreg[kk], kk == 0 ? zero : s[kb], 0, 0, 0);
+      }
+    }
+  };
+  auto wait_dma = [&]() { __builtin_amdgcn_s_waitcnt(0x0F70); };  // vmcnt(0)
+
+  f32x16 oacc[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[i][r] = 0.f;
+  float mc = -INFINITY;
+  float l_run = 0.f;
+  const float c = a.scale_log2;
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+
+  f32x16 s[NKB], sn[NKB];
+  int full_cur = 1;
+  TileStream ks;
+  stream_init<BN, MODE>(ks, a, list, cnt, 0);
+  TileD tprev;
+  if (ntiles > 0) {
+    const TileD t0 = stream_tile<BN, MODE>(ks, a, L);
+    stream_next<BN, MODE>(ks, a, list, cnt);
+    const TileD t1 = stream_tile<BN, MODE>(ks, a, L);
+    stream_next<BN, MODE>(ks, a, list, cnt);
+    load_k(t0, 0);
+    load_v(t0, 0);
+    load_k(t1, 1);
+    full_cur = t0.full;
+    tprev = t1;
+  }
+  wait_dma();
+  __syncthreads();
+  if (ntiles > 0) qk(0, s);
+  __syncthreads();
+
+  auto step = [&](const int st, f32x16 (&cur)[NKB], f32x16 (&nxt)[NKB]) {
+    // K of tile i+2 into the stage of tile i (its K was read last step);
+    // V of tile i+1 into the other stage (its V was read last step).
+    const TileD tk = stream_tile<BN, MODE>(ks, a, L);
+    stream_next<BN, MODE>(ks, a, list, cnt);
+    const TileD tv = tprev;
+    tprev = tk;
+    load_k(tk, st);
+    load_v(tv, st ^ 1);
+
+    if (!full_cur) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const unsigned f4 = kval[st][(kb * 32 + 8 * g + 4 * half) >> 2];
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (((f4 >> (8 * i)) & 0xffu) == 0u) cur[kb][4 * g + i] = -INFINITY;
+        }
+    }
+
+    qk(st ^ 1, nxt);
+
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, cur[kb][r]);
+    mx = half_max(mx) * c;
+    const bool need = mx > mc + kRescale;
+    const float mc_new = need ? mx : mc;
+    const float alpha = need ? __builtin_amdgcn_exp2f(mc - mc_new) : 1.f;
+    mc = mc_new;
+    l_run *= alpha;
+    const float nm = (mc == -INFINITY) ? 0.f : -mc;
+
+    bf16x8 pb[PVSTEPS];
+#pragma unroll
+    for (int kk = 0; kk < PVSTEPS; ++kk) {
+#pragma unroll
+      for (int j = 0; j < 8; j += 2) {
+        const float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(cur[kk >> 1][8 * (kk & 1) + j], c, nm));
+        const float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(cur[kk >> 1][8 * (kk & 1) + j + 1], c, nm));
+        const bf16x2 p2 = {(__bf16)x0, (__bf16)x1};
+        l_run = __builtin_amdgcn_fdot2_f32_bf16(p2, ones, l_run, false);
+        pb[kk][j] = p2[0];
+        pb[kk][j + 1] = p2[1];
+      }
+    }
+
+    if (__ballot(need && (l_run == l_run)) != 0ull) {
+#pragma unroll
+      for (int i = 0; i < NDB; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
+    }
+
+#pragma unroll
+    for (int kk = 0; kk < PVSTEPS; ++kk) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        lds_u8* const vb = (lds_u8*)vbuf(st) + vra[db] + 16 * kk * 256;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)vb);
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + 8 * 256));
+        const s16x4 both[2] = {lo, hi};
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, both), pb[kk], oacc[db], 0, 0, 0);
+      }
+    }
+
+    full_cur = tv.full;
+    wait_dma();
+    __syncthreads();
+  };
+
+  int it = 0;
+  for (; it + 1 < ntiles; it += 2) {
+    step(0, s, sn);
+    step(1, sn, s);
+  }
+  if (it < ntiles) step(0, s, sn);
+
+  const float l_tot = half_sum(l_run);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (q_in_blk) {
+    float* orow = Oh + (size_t)qrow * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = 32 * db + 8 * g + 4 * half;
+        float4 v;
+        if (q_valid) {
+          v = make_float4(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv, oacc[db][4 * g + 2] * inv,
+                          oacc[db][4 * g + 3] * inv);
+        } else {
+          v = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+        *(float4*)(orow + d0) = v;
+      }
+  }
+}
+
 template <int D, int BN>
 hipError_t launch_mode(const AttnArgs& a, hipStream_t s) {
   dim3 grid(a.total_tiles), block(kThreads);
@@ -507,9 +805,20 @@ hipError_t launch_mode(const AttnArgs& a, hipStream_t s) {
 
 }  // namespace
 
+hipError_t launch_d128(const AttnArgs& a, hipStream_t s) {
+  dim3 grid(a.total_tiles), block(kThreads);
+  if (a.dense)
+    hipLaunchKernelGGL(bsa_fwd_d128_kernel<MODE_DENSE>, grid, block, 0, s, a);
+  else if (a.block_k >= 64)
+    hipLaunchKernelGGL(bsa_fwd_d128_kernel<MODE_LIST>, grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL(bsa_fwd_d128_kernel<MODE_SMALL>, grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_attn_bf16(const AttnArgs& a, int d, hipStream_t s) {
   if (a.total_tiles == 0) return hipSuccess;
-  return d == 128 ? launch_mode<128, 64>(a, s) : launch_mode<64, 128>(a, s);
+  return d == 128 ? launch_d128(a, s) : launch_mode<64, 128>(a, s);
 }
 
 }  // namespace lvsa
