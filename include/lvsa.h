@@ -119,7 +119,8 @@ int draft_grid_info(int T, int H, int grid_w, int pool_h, int pool_w, double spa
 
 /* Host-only. Bytes of device workspace draft_mask_and_perm needs:
  * pooled Q̄ and K̄, each [heads, nb, d] fp32, at byte offsets 0 and
- * heads*nb*d*4. Returns 0 for invalid arguments. */
+ * heads*nb*d*4, then K̄ transposed, [heads, d, nb] fp32, at byte offset
+ * 2*heads*nb*d*4. Returns 0 for invalid arguments. */
 size_t draft_workspace_bytes(int heads, int T, int H, int grid_w, int d, int pool_h, int pool_w);
 
 /* Full Draft mask builder on Q, K (and the reorder of Q, K, V).
@@ -130,7 +131,7 @@ size_t draft_workspace_bytes(int heads, int T, int H, int grid_w, int d, int poo
  *   q_perm, k_perm, v_perm  out [heads, N_pad, d] of dtype dt: the reordered
  *               tensors, pads zero. All three NULL to skip the reorder.
  *   workspace   device buffer of ws_bytes >= draft_workspace_bytes(...);
- *               holds Q̄ and K̄ on return (layout above).
+ *               holds Q̄, K̄ and K̄ᵀ on return (layout above).
  * Requires block size <= 1024 and nb <= 4096. */
 int draft_mask_and_perm(const void* q, const void* k, const void* v, int dt, int heads, int T, int H, int grid_w,
                         int d, int pool_h, int pool_w, double sparsity, int32_t* kv_idx, int32_t* kv_cnt,

@@ -58,7 +58,7 @@ def test_grid_info_matches_oracle(lib, T, H, W, ph, pw, sp):
     info = _lib.draft_grid_info(T, H, W, ph, pw, sp)
     g = oracle.draft_grid(T, H, W, ph, pw)
     assert info == {"nb": g.nb, "n_pad": g.N_pad, "block_size": g.block_size, "k": oracle.topk_count(sp, g.nb)}
-    assert _lib.draft_workspace_bytes(24, T, H, W, 128, ph, pw) == 2 * 24 * g.nb * 128 * 4
+    assert _lib.draft_workspace_bytes(24, T, H, W, 128, ph, pw) == 3 * 24 * g.nb * 128 * 4
 
 
 def test_grid_info_rejects(lib):

@@ -43,6 +43,10 @@ DRAFT_CASES = [
     (3, 45, 80, 8, 16, 2, 128, 0.9, "bf16"),
     (2, 13, 21, 8, 16, 3, 64, 0.7, "bf16"),
     (2, 9, 30, 4, 8, 2, 64, 0.0, "f32"),
+    # nb = 1560, 2080 and 4096: the map kernel's 4- and 2-row workgroups and the largest grid
+    (3, 40, 52, 2, 2, 1, 64, 0.8, "f32"),
+    (4, 40, 52, 2, 2, 1, 64, 0.95, "f32"),
+    (1, 128, 128, 2, 2, 1, 64, 0.9, "f32"),
 ]
 
 
@@ -100,6 +104,23 @@ def test_draft_ties_and_zero():
     out = _lib.draft_mask_and_perm(to_dev(z), to_dev(z), to_dev(z), T, H, W, 4, 8, 0.5)
     k = out["info"]["k"]
     assert np.array_equal(to_host(out["kv_idx"]), np.tile(np.arange(k, dtype=np.int32), (heads, out["info"]["nb"], 1)))
+
+
+def test_draft_ties_cut_by_k():
+    """K constant within each frame: a frame's blocks all tie, and k cuts
+    through a tie group, so the lower block indices of that group are kept."""
+    T, H, W, heads, d, sp = 5, 12, 16, 2, 64, 0.7
+    rng = np.random.default_rng(8)
+    q = rng.standard_normal((heads, T * H * W, d)).astype(np.float32)
+    kf = rng.standard_normal((heads, T, 1, d)).astype(np.float32)
+    k = np.ascontiguousarray(np.broadcast_to(kf, (heads, T, H * W, d)).reshape(heads, T * H * W, d))
+    note("draft frame ties")
+    out = _lib.draft_mask_and_perm(to_dev(q), to_dev(k), to_dev(k), T, H, W, 4, 4, sp)
+    g = oracle.draft_grid(T, H, W, 4, 4)
+    kv, cnt, *_ = oracle.draft_mask(q, k, g, sp)
+    assert g.nb % T == 0 and (oracle.topk_count(sp, g.nb) % (g.nb // T)) != 0
+    assert np.array_equal(to_host(out["kv_idx"]), kv)
+    assert np.array_equal(to_host(out["kv_cnt"]), cnt)
 
 
 def test_draft_mask_only_without_reorder():

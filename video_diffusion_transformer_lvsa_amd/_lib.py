@@ -180,7 +180,7 @@ def draft_mask_and_perm(q, k, v, T: int, H: int, grid_w: int, pool_h: int, pool_
         _ptr(out.get("q_perm")), _ptr(out.get("k_perm")), _ptr(out.get("v_perm")), _ptr(ws), ws_bytes,
         _stream(stream)))
     out["qbar"] = ws[: heads * nb * d].view(heads, nb, d)
-    out["kbar"] = ws[heads * nb * d :].view(heads, nb, d)
+    out["kbar"] = ws[heads * nb * d : 2 * heads * nb * d].view(heads, nb, d)
     return out
 
 

@@ -217,7 +217,7 @@ size_t draft_workspace_bytes(int heads, int T, int H, int grid_w, int d, int poo
   lvsa::DraftGeom g;
   if (geom(T, H, grid_w, pool_h, pool_w, &g)) return 0;
   if (heads < 1 || d < 1) return 0;
-  return 2 * (size_t)heads * g.nb * d * sizeof(float);
+  return 3 * (size_t)heads * g.nb * d * sizeof(float);
 }
 
 int draft_mask_and_perm(const void* q, const void* k, const void* v, int dt, int heads, int T, int H, int grid_w,
@@ -245,19 +245,21 @@ int draft_mask_and_perm(const void* q, const void* k, const void* v, int dt, int
   if (!aligned16(q) || !aligned16(k) || (v && !aligned16(v)) || !aligned16(q_perm) || !aligned16(k_perm) ||
       !aligned16(v_perm) || !aligned16(workspace))
     return fail(LVSA_EINVAL, "tensors and workspace must be 16-byte aligned");
-  const size_t need = 2 * (size_t)heads * g.nb * d * sizeof(float);
+  const size_t need = 3 * (size_t)heads * g.nb * d * sizeof(float);
   if (!workspace || ws_bytes < need) return fail(LVSA_ENOMEM, "workspace %zu bytes < required %zu", ws_bytes, need);
   rc = check_device();
   if (rc) return rc;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   float* qbar = static_cast<float*>(workspace);
   float* kbar = qbar + (size_t)heads * g.nb * d;
+  float* kbarT = kbar + (size_t)heads * g.nb * d;
   rc = launched(lvsa::launch_draft_perm(g, perm, inv_perm, block_valid, s), "draft perm launch");
   if (rc) return rc;
-  rc = launched(lvsa::launch_draft_pool_gather(g, heads, d, dt, q, k, v, qbar, kbar, q_perm, k_perm, v_perm, s),
+  rc = launched(lvsa::launch_draft_pool_gather(g, heads, d, dt, q, k, v, qbar, kbar, kbarT, q_perm, k_perm, v_perm,
+                                               s),
                 "draft pool launch");
   if (rc) return rc;
-  return launched(lvsa::launch_draft_select(qbar, kbar, heads, g.nb, d, topk, kv_idx, kv_cnt, s),
+  return launched(lvsa::launch_draft_select(qbar, kbarT, heads, g.nb, d, topk, kv_idx, kv_cnt, s),
                   "draft select launch");
 }
 

@@ -66,8 +66,9 @@ __global__ __launch_bounds__(256) void draft_pool_gather_kernel(DraftGeom g, int
                                                                 const void* __restrict__ q,
                                                                 const void* __restrict__ k,
                                                                 const void* __restrict__ v, float* __restrict__ qbar,
-                                                                float* __restrict__ kbar, void* __restrict__ q_perm,
-                                                                void* __restrict__ k_perm, void* __restrict__ v_perm) {
+                                                                float* __restrict__ kbar, float* __restrict__ kbarT,
+                                                                void* __restrict__ q_perm, void* __restrict__ k_perm,
+                                                                void* __restrict__ v_perm) {
   constexpr int CH = BF16 ? 8 : 4;  // channels per 16-byte chunk
   const int LPR = d / CH;           // lanes per row
   const int gpb = blockDim.x / LPR; // groups per workgroup
@@ -123,124 +124,126 @@ __global__ __launch_bounds__(256) void draft_pool_gather_kernel(DraftGeom g, int
     float* out = bar + ((size_t)h * g.nb + b) * d + lane * CH;
 #pragma unroll
     for (int i = 0; i < CH; ++i) out[i] = __fdiv_rn(acc[i], cnt);
+    if (which == 1) {  // K̄ᵀ [heads, d, nb] for coalesced reads by the map kernel
+      float* outT = kbarT + (size_t)h * d * g.nb + (size_t)(lane * CH) * g.nb + b;
+#pragma unroll
+      for (int i = 0; i < CH; ++i) outT[(size_t)i * g.nb] = __fdiv_rn(acc[i], cnt);
+    }
   }
 }
 
 // ---------------------------------------------------------------------------
-// Draft map + top-k. One workgroup owns R query-block rows of one head:
+// Draft map + top-k. One workgroup owns R query-block rows of one head.
 //  1. s[r][j] = fold_c fl(acc + fl(q̄[r][c] * k̄[j][c])) for every KV block j;
-//  2. each score becomes a 64-bit key (descending score, then ascending j;
-//     -0 canonicalised to +0) and each row is bitonic-sorted in LDS;
-//  3. the first k keys mark their blocks; a workgroup scan writes the marked
-//     block ids in ascending order.
+//     thread t owns columns t, t + 256, ... and reads k̄ from its transposed
+//     copy, so a wave's loads are contiguous, while the R query values of a
+//     channel are one LDS broadcast. Each score is stored in LDS as an
+//     order-preserving unsigned code (-0 folded into +0).
+//  2. One wave per row selects the k largest codes, ties to the lower block
+//     index: a 32-step bisection finds the k-th largest code tau; the row
+//     keeps every code > tau and the first (k - #{> tau}) codes == tau in
+//     index order, written out in ascending index order with ballots.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ unsigned long long score_key(float s, int j) {
+__device__ __forceinline__ unsigned int order_code(float s) {
   unsigned int bits = __float_as_uint(s);
   if (bits == 0x80000000u) bits = 0u;
-  const unsigned int asc = (bits & 0x80000000u) ? ~bits : (bits | 0x80000000u);
-  return ((unsigned long long)(~asc) << 32) | (unsigned int)j;
+  return (bits & 0x80000000u) ? ~bits : (bits | 0x80000000u);
 }
 
+__device__ __forceinline__ int lanes_below(unsigned long long mask) {
+  return (int)__builtin_amdgcn_mbcnt_hi((unsigned int)(mask >> 32),
+                                        __builtin_amdgcn_mbcnt_lo((unsigned int)mask, 0u));
+}
+
+template <int R>
 __global__ __launch_bounds__(256) void draft_select_kernel(const float* __restrict__ qbar,
-                                                           const float* __restrict__ kbar, int heads, int nb, int d,
-                                                           int topk, int nbp, int R, int32_t* __restrict__ kv_idx,
+                                                           const float* __restrict__ kbarT, int heads, int nb, int d,
+                                                           int topk, int32_t* __restrict__ kv_idx,
                                                            int32_t* __restrict__ kv_cnt) {
-  extern __shared__ unsigned long long smem[];
-  unsigned long long* keys = smem;                      // [R][nbp]
-  float* qs = (float*)(keys + (size_t)R * nbp);         // [R][d]
-  unsigned char* sel = (unsigned char*)(qs + R * d);    // [R][nbp]
-  __shared__ int scan[256];
+  extern __shared__ unsigned int codes[];  // [R][nb64]
+  __shared__ float qsT[128 * R];           // [d][R]; d <= 128 (checked on the host)
 
   const int tid = threadIdx.x;
+  const int nb64 = (nb + 63) & ~63;
   const int rows_per_head = (nb + R - 1) / R;
   const int h = blockIdx.x / rows_per_head;
   const int i0 = (blockIdx.x - h * rows_per_head) * R;
   const int nr = min(R, nb - i0);
 
   for (int e = tid; e < R * d; e += blockDim.x) {
-    const int r = e / d;
-    qs[e] = r < nr ? qbar[((size_t)h * nb + i0 + r) * d + (e - r * d)] : 0.f;
+    const int c = e / R, r = e - c * R;
+    qsT[e] = r < nr ? qbar[((size_t)h * nb + i0 + r) * d + c] : 0.f;
   }
   __syncthreads();
 
-  const float* kh = kbar + (size_t)h * nb * d;
-  for (int j = tid; j < nbp; j += blockDim.x) {
-    if (j < nb) {
-      float acc[8];
+  const float* kh = kbarT + (size_t)h * d * nb;
+  const int ngroups = (nb + 255) / 256;
+  for (int m0 = 0; m0 < ngroups; m0 += 4) {
+    float acc[4][R];
 #pragma unroll
-      for (int r = 0; r < 8; ++r) acc[r] = 0.f;
-      const float4* kr = (const float4*)(kh + (size_t)j * d);
-      for (int c4 = 0; c4 < d / 4; ++c4) {
-        const float4 kv = kr[c4];
-        const float kc[4] = {kv.x, kv.y, kv.z, kv.w};
+    for (int m = 0; m < 4; ++m)
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+      for (int r = 0; r < R; ++r) acc[m][r] = 0.f;
+#pragma unroll 4
+    for (int c = 0; c < d; ++c) {
+      float qv[R];
 #pragma unroll
-          for (int r = 0; r < 8; ++r)
-            if (r < R) acc[r] = __fadd_rn(acc[r], __fmul_rn(qs[r * d + 4 * c4 + u], kc[u]));
-        }
+      for (int r = 0; r < R; ++r) qv[r] = qsT[c * R + r];
+      const float* kc = kh + (size_t)c * nb;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int j = tid + 256 * (m0 + m);
+        const float kv = j < nb ? kc[j] : 0.f;
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[m][r] = __fadd_rn(acc[m][r], __fmul_rn(qv[r], kv));
       }
+    }
 #pragma unroll
-      for (int r = 0; r < 8; ++r)
-        if (r < R) keys[(size_t)r * nbp + j] = score_key(acc[r], j);
-    } else {
-      for (int r = 0; r < R; ++r) keys[(size_t)r * nbp + j] = ~0ull;
-    }
-  }
-  __syncthreads();
-
-  // Ascending bitonic sort of each row.
-  const int half_n = nbp >> 1;
-  for (int kk = 2; kk <= nbp; kk <<= 1) {
-    for (int jj = kk >> 1; jj > 0; jj >>= 1) {
-      for (int e = tid; e < R * half_n; e += blockDim.x) {
-        const int r = e / half_n, ip = e - r * half_n;
-        const int i = (ip / jj) * 2 * jj + (ip % jj);
-        const int p = i + jj;
-        unsigned long long* row = keys + (size_t)r * nbp;
-        const unsigned long long x = row[i], y = row[p];
-        const bool up = (i & kk) == 0;
-        if ((x > y) == up) {
-          row[i] = y;
-          row[p] = x;
-        }
+    for (int m = 0; m < 4; ++m) {
+      const int j = tid + 256 * (m0 + m);
+      if (j < nb64) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) codes[r * nb64 + j] = j < nb ? order_code(acc[m][r]) : 0u;
       }
-      __syncthreads();
     }
-  }
-
-  for (int e = tid; e < R * nbp; e += blockDim.x) sel[e] = 0;
-  __syncthreads();
-  for (int e = tid; e < R * topk; e += blockDim.x) {
-    const int r = e / topk, i = e - r * topk;
-    const unsigned int j = (unsigned int)(keys[(size_t)r * nbp + i] & 0xffffffffu);
-    if (r < nr && j < (unsigned int)nb) sel[r * nbp + j] = 1;
   }
   __syncthreads();
 
-  // Ascending compaction of the marked blocks, one row at a time.
-  const int per = (nbp + blockDim.x - 1) / blockDim.x;
-  for (int r = 0; r < nr; ++r) {
-    const int j0 = tid * per;
-    int c = 0;
-    for (int u = 0; u < per; ++u)
-      if (j0 + u < nb) c += sel[r * nbp + j0 + u];
-    scan[tid] = c;
-    __syncthreads();
-    for (int off = 1; off < (int)blockDim.x; off <<= 1) {
-      const int add = tid >= off ? scan[tid - off] : 0;
-      __syncthreads();
-      scan[tid] += add;
-      __syncthreads();
+  const int w = tid >> 6, lane = tid & 63;
+  const int nch = nb64 >> 6;
+  for (int r = w; r < nr; r += (int)(blockDim.x >> 6)) {
+    const unsigned int* row = codes + r * nb64;
+    unsigned int tau = 0u;
+    for (int bit = 31; bit >= 0; --bit) {
+      const unsigned int cand = tau | (1u << bit);
+      int cnt = 0;
+      for (int m = 0; m < nch; ++m) {
+        const int j = 64 * m + lane;
+        cnt += __popcll(__ballot(j < nb && row[j] >= cand));
+      }
+      if (cnt >= topk) tau = cand;
     }
-    int pos = scan[tid] - c;
+    int greater = 0;
+    for (int m = 0; m < nch; ++m) {
+      const int j = 64 * m + lane;
+      greater += __popcll(__ballot(j < nb && row[j] > tau));
+    }
+    const int need_eq = topk - greater;
     int32_t* out = kv_idx + ((size_t)h * nb + i0 + r) * topk;
-    for (int u = 0; u < per; ++u) {
-      const int j = j0 + u;
-      if (j < nb && sel[r * nbp + j]) out[pos++] = j;
+    int eq_seen = 0, base = 0;
+    for (int m = 0; m < nch; ++m) {
+      const int j = 64 * m + lane;
+      const bool valid = j < nb;
+      const unsigned int a = row[j];
+      const bool eq = valid && a == tau;
+      const unsigned long long eqm = __ballot(eq);
+      const bool take = valid && (a > tau || (eq && eq_seen + lanes_below(eqm) < need_eq));
+      const unsigned long long tm = __ballot(take);
+      if (take) out[base + lanes_below(tm)] = j;
+      eq_seen += __popcll(eqm);
+      base += __popcll(tm);
     }
-    if (tid == 0) kv_cnt[(size_t)h * nb + i0 + r] = topk;
-    __syncthreads();
+    if (lane == 0) kv_cnt[(size_t)h * nb + i0 + r] = topk;
   }
 }
 
@@ -287,33 +290,35 @@ hipError_t launch_draft_perm(const DraftGeom& g, int32_t* perm, int32_t* inv_per
 }
 
 hipError_t launch_draft_pool_gather(const DraftGeom& g, int heads, int d, int dt, const void* q, const void* k,
-                                    const void* v, float* qbar, float* kbar, void* q_perm, void* k_perm,
-                                    void* v_perm, hipStream_t s) {
+                                    const void* v, float* qbar, float* kbar, float* kbarT, void* q_perm,
+                                    void* k_perm, void* v_perm, hipStream_t s) {
   const int ch = dt == 1 ? 8 : 4;
   const int lpr = d / ch;
   const int gpb = 256 / lpr;
   const int groups = heads * g.nb;
   dim3 grid((groups + gpb - 1) / gpb, v_perm ? 3 : 2), block(256);
   if (dt == 1)
-    hipLaunchKernelGGL(draft_pool_gather_kernel<true>, grid, block, 0, s, g, heads, d, q, k, v, qbar, kbar, q_perm,
-                       k_perm, v_perm);
+    hipLaunchKernelGGL(draft_pool_gather_kernel<true>, grid, block, 0, s, g, heads, d, q, k, v, qbar, kbar, kbarT,
+                       q_perm, k_perm, v_perm);
   else
-    hipLaunchKernelGGL(draft_pool_gather_kernel<false>, grid, block, 0, s, g, heads, d, q, k, v, qbar, kbar, q_perm,
-                       k_perm, v_perm);
+    hipLaunchKernelGGL(draft_pool_gather_kernel<false>, grid, block, 0, s, g, heads, d, q, k, v, qbar, kbar, kbarT,
+                       q_perm, k_perm, v_perm);
   return hipGetLastError();
 }
 
-hipError_t launch_draft_select(const float* qbar, const float* kbar, int heads, int nb, int d, int topk,
+hipError_t launch_draft_select(const float* qbar, const float* kbarT, int heads, int nb, int d, int topk,
                                int32_t* kv_idx, int32_t* kv_cnt, hipStream_t s) {
-  int nbp = 1;
-  while (nbp < nb) nbp <<= 1;
-  int R = 4096 / nbp;
-  R = R < 1 ? 1 : (R > 8 ? 8 : R);
-  const size_t shm = (size_t)R * nbp * 8 + (size_t)R * d * 4 + (size_t)R * nbp;
-  const int rows_per_head = (nb + R - 1) / R;
-  dim3 grid(heads * rows_per_head), block(256);
-  hipLaunchKernelGGL(draft_select_kernel, grid, block, shm, s, qbar, kbar, heads, nb, d, topk, nbp, R, kv_idx,
-                     kv_cnt);
+  // Rows per workgroup so that the score codes take at most 32 KB of LDS.
+  const int nb64 = (nb + 63) & ~63;
+  const int R = nb64 <= 1024 ? 8 : (nb64 <= 2048 ? 4 : 2);
+  const size_t shm = (size_t)R * nb64 * sizeof(unsigned int);
+  dim3 grid(heads * ((nb + R - 1) / R)), block(256);
+  if (R == 8)
+    hipLaunchKernelGGL(draft_select_kernel<8>, grid, block, shm, s, qbar, kbarT, heads, nb, d, topk, kv_idx, kv_cnt);
+  else if (R == 4)
+    hipLaunchKernelGGL(draft_select_kernel<4>, grid, block, shm, s, qbar, kbarT, heads, nb, d, topk, kv_idx, kv_cnt);
+  else
+    hipLaunchKernelGGL(draft_select_kernel<2>, grid, block, shm, s, qbar, kbarT, heads, nb, d, topk, kv_idx, kv_cnt);
   return hipGetLastError();
 }
 

@@ -55,9 +55,9 @@ hipError_t launch_draft_perm(const DraftGeom& g, int32_t* perm, int32_t* inv_per
 // Pools q and k (dtype 0 = f32, 1 = bf16) into qbar/kbar and, when the
 // *_perm pointers are non-NULL, writes the reordered tensors.
 hipError_t launch_draft_pool_gather(const DraftGeom& g, int heads, int d, int dt, const void* q, const void* k,
-                                    const void* v, float* qbar, float* kbar, void* q_perm, void* k_perm,
-                                    void* v_perm, hipStream_t s);
-hipError_t launch_draft_select(const float* qbar, const float* kbar, int heads, int nb, int d, int topk,
+                                    const void* v, float* qbar, float* kbar, float* kbarT, void* q_perm,
+                                    void* k_perm, void* v_perm, hipStream_t s);
+hipError_t launch_draft_select(const float* qbar, const float* kbarT, int heads, int nb, int d, int topk,
                                int32_t* kv_idx, int32_t* kv_cnt, hipStream_t s);
 hipError_t launch_draft_scores(const float* qbar, const float* kbar, int heads, int nb_q, int nb_k, int d,
                                float* scores, hipStream_t s);
