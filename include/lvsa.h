@@ -148,7 +148,9 @@ int draft_scores(const float* qbar, const float* kbar, int heads, int nb_q, int 
  * dst_to_src[i] < 0 or >= n_src. src [heads, n_src, d], dst [heads, n_dst, d],
  * element type dt (bf16 or fp32); the map is [n_dst] int32. With
  * dst_to_src = inv_perm it scatters a reordered O back to token order; with
- * perm it builds a reordered tensor. src and dst must not overlap. */
+ * perm it builds a reordered tensor. src and dst must not overlap; d*esize
+ * must be a multiple of 16 bytes; one head of src or dst must hold fewer
+ * than 2^31 16-byte chunks (LVSA_EINVAL otherwise). */
 int token_permute(const void* src, void* dst, int dt, int heads, int n_src, int n_dst, int d,
                   const int32_t* dst_to_src, void* stream);
 

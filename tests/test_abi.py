@@ -115,6 +115,7 @@ def test_mask_and_permute_validation(lib):
     assert tp(FAKE, FAKE, 1, 2, 10, 10, 128, None, None) == _lib.LVSA_EINVAL
     assert tp(FAKE, FAKE, 1, 2, 10, 10, 128, FAKE, None) == _lib.LVSA_EINVAL  # overlap
     assert tp(FAKE, FAKE, 1, 2, 10, 0, 128, FAKE, None) == 0
+    assert tp(FAKE, FAKE, 1, 2, 1 << 27, 10, 128, FAKE, None) == _lib.LVSA_EINVAL  # 2^31 chunks per head
     dm = lib.draft_mask_and_perm
     base = [FAKE, FAKE, FAKE, 1, 2, 2, 10, 16, 128, 4, 8, 0.5, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE]
     need = lib.draft_workspace_bytes(2, 2, 10, 16, 128, 4, 8)

@@ -286,6 +286,10 @@ int token_permute(const void* src, void* dst, int dt, int heads, int n_src, int 
   if (heads < 0 || n_src < 0 || n_dst < 0 || d < 1) return fail(LVSA_EINVAL, "bad sizes");
   if ((d * esize) % 16 != 0 || d > 4096) return fail(LVSA_EUNSUPPORTED, "row of %d elements is not a multiple of 16 bytes", d);
   if ((long long)heads * n_dst == 0) return LVSA_OK;
+  const long long cpr = (long long)d * esize / 16;
+  if ((long long)n_src * cpr >= (1ll << 31) || (long long)n_dst * cpr >= (1ll << 31) ||
+      (long long)heads * ((n_dst * cpr + 1023) / 1024) >= (1ll << 31))
+    return fail(LVSA_EINVAL, "a head of %d or %d rows of %d elements exceeds 2^31 16-byte chunks", n_src, n_dst, d);
   if (!src || !dst || !dst_to_src) return fail(LVSA_EINVAL, "src, dst, dst_to_src must be non-NULL");
   if (!aligned16(src) || !aligned16(dst)) return fail(LVSA_EINVAL, "src and dst must be 16-byte aligned");
   const char* s0 = static_cast<const char*>(src);

@@ -49,16 +49,20 @@ __global__ void draft_perm_kernel(DraftGeom g, int32_t* __restrict__ perm, int32
 }
 
 // ---------------------------------------------------------------------------
-// Pool (Q, K) + reorder (Q, K, V). One group of LPR lanes owns one
-// (tensor, head, block); each lane owns CH consecutive channels and walks
-// the block's slots in order, so every channel's sum is a sequential fold.
+// Pool (Q, K) + reorder (Q, K, V). One workgroup owns one (tensor, head,
+// block). The block's rows are moved in stages of 4 rounds; in a round the
+// 256 threads load 4 KB of rows as 16-byte chunks (rows of one pool-tile line
+// are contiguous in the source) and store them to the block's slots in the
+// reordered tensor, pads as zeros. For Q and K a stage is also staged in LDS,
+// where lane c folds channel c over the stage's slots in slot order, so every
+// channel's sum is one sequential fold across the whole block.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void unpack(const u32x4& v, float (&x)[8]) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    x[2 * i] = __uint_as_float(v[i] << 16);
-    x[2 * i + 1] = __uint_as_float(v[i] & 0xffff0000u);
-  }
+__device__ __forceinline__ int xcd_local(int w, int G) {
+  // Workgroup w runs on XCD w % 8: give each XCD a contiguous range of work
+  // items so that neighbouring blocks share an L2 (and K-bar-transposed
+  // columns merge there before they are written back).
+  const int xcd = w & 7, idx = w >> 3, q8 = G >> 3, r8 = G & 7;
+  return (xcd < r8 ? xcd * (q8 + 1) : r8 * (q8 + 1) + (xcd - r8) * q8) + idx;
 }
 
 template <bool BF16>
@@ -69,18 +73,19 @@ __global__ __launch_bounds__(256) void draft_pool_gather_kernel(DraftGeom g, int
                                                                 float* __restrict__ kbar, float* __restrict__ kbarT,
                                                                 void* __restrict__ q_perm, void* __restrict__ k_perm,
                                                                 void* __restrict__ v_perm) {
-  constexpr int CH = BF16 ? 8 : 4;  // channels per 16-byte chunk
-  const int LPR = d / CH;           // lanes per row
-  const int gpb = blockDim.x / LPR; // groups per workgroup
-  const int which = blockIdx.y;     // 0 = Q, 1 = K, 2 = V
-  const int grp = blockIdx.x * gpb + threadIdx.x / LPR;
-  const int lane = threadIdx.x % LPR;
-  if (grp >= heads * g.nb) return;
-  const int h = grp / g.nb, b = grp - h * g.nb;
+  constexpr int ES = BF16 ? 2 : 4;
+  constexpr int ROUNDS = 4;
+  __shared__ u32x4 stage[ROUNDS * 256];  // 16 KB
+
+  const int G = (v_perm ? 3 : 2) * heads * g.nb;
+  const int L = xcd_local(blockIdx.x, G);
+  const int which = L / (heads * g.nb);  // 0 = Q, 1 = K, 2 = V
+  const int rem = L - which * heads * g.nb;
+  const int h = rem / g.nb, b = rem - h * g.nb;
 
   const void* src = which == 0 ? q : (which == 1 ? k : v);
   void* dst = which == 0 ? q_perm : (which == 1 ? k_perm : v_perm);
-  float* bar = which == 0 ? qbar : (which == 1 ? kbar : nullptr);
+  const bool pool = which < 2;
 
   const int t = b / (g.nbh * g.nbw);
   const int rb = b - t * (g.nbh * g.nbw);
@@ -88,47 +93,57 @@ __global__ __launch_bounds__(256) void draft_pool_gather_kernel(DraftGeom g, int
   const int vh = min(g.ph, g.H - hb * g.ph);
   const int vw = min(g.pw, g.W - wb * g.pw);
   const int nv = vh * vw;
-
-  const u32x4* S = (const u32x4*)src + (size_t)h * g.n * LPR;
-  u32x4* Dd = dst ? (u32x4*)dst + ((size_t)h * g.n_pad + (size_t)b * g.bs) * LPR : nullptr;
-
-  float acc[CH];
-#pragma unroll
-  for (int i = 0; i < CH; ++i) acc[i] = 0.f;
-
   const int tok0 = (t * g.H + hb * g.ph) * g.W + wb * g.pw;
-#pragma unroll 4
-  for (int slot = 0; slot < nv; ++slot) {
-    const int hi = slot / vw, wi = slot - hi * vw;
-    const int tok = tok0 + hi * g.W + wi;
-    const u32x4 x = S[(size_t)tok * LPR + lane];
-    if (Dd) Dd[(size_t)slot * LPR + lane] = x;
-    if (bar) {
-      if (BF16) {
-        float f[8];
-        unpack(x, f);
+
+  const int rowc = d * ES / 16;          // 16-byte chunks per row
+  const int rpr = 256 / rowc;            // rows per round
+  const int tid = threadIdx.x;
+  const int sub = tid / rowc, ch = tid - sub * rowc;
+  const u32x4* S = (const u32x4*)src + (size_t)h * g.n * rowc;
+  u32x4* Dd = dst ? (u32x4*)dst + ((size_t)h * g.n_pad + (size_t)b * g.bs) * rowc : nullptr;
+
+  float acc = 0.f;
+  for (int s0 = 0; s0 < g.bs; s0 += ROUNDS * rpr) {
+    u32x4 x[ROUNDS];
 #pragma unroll
-        for (int i = 0; i < CH; ++i) acc[i] = __fadd_rn(acc[i], f[i]);
-      } else {
-#pragma unroll
-        for (int i = 0; i < CH; ++i) acc[i] = __fadd_rn(acc[i], __uint_as_float(x[i]));
+    for (int i = 0; i < ROUNDS; ++i) {
+      const int slot = s0 + i * rpr + sub;
+      x[i] = u32x4{0u, 0u, 0u, 0u};
+      if (slot < nv) {
+        const int hi = slot / vw, wi = slot - hi * vw;
+        x[i] = S[(size_t)(tok0 + hi * g.W + wi) * rowc + ch];
       }
     }
-  }
-  if (Dd) {
-    const u32x4 z = {0u, 0u, 0u, 0u};
-    for (int slot = nv; slot < g.bs; ++slot) Dd[(size_t)slot * LPR + lane] = z;
-  }
-  if (bar) {
-    const float cnt = (float)nv;
-    float* out = bar + ((size_t)h * g.nb + b) * d + lane * CH;
+    if (Dd) {
 #pragma unroll
-    for (int i = 0; i < CH; ++i) out[i] = __fdiv_rn(acc[i], cnt);
-    if (which == 1) {  // K̄ᵀ [heads, d, nb] for coalesced reads by the map kernel
-      float* outT = kbarT + (size_t)h * d * g.nb + (size_t)(lane * CH) * g.nb + b;
-#pragma unroll
-      for (int i = 0; i < CH; ++i) outT[(size_t)i * g.nb] = __fdiv_rn(acc[i], cnt);
+      for (int i = 0; i < ROUNDS; ++i) {
+        const int slot = s0 + i * rpr + sub;
+        if (slot < g.bs) Dd[(size_t)slot * rowc + ch] = x[i];
+      }
     }
+    if (pool) {
+#pragma unroll
+      for (int i = 0; i < ROUNDS; ++i) stage[i * 256 + tid] = x[i];
+      __syncthreads();
+      if (tid < d) {
+        const int n_here = min(ROUNDS * rpr, nv - s0);
+        const unsigned char* base = (const unsigned char*)stage + tid * ES;
+        for (int r = 0; r < n_here; ++r) {
+          float xv;
+          if (BF16)
+            xv = __uint_as_float((unsigned int)*(const unsigned short*)(base + (size_t)r * d * ES) << 16);
+          else
+            xv = *(const float*)(base + (size_t)r * d * ES);
+          acc = __fadd_rn(acc, xv);
+        }
+      }
+      __syncthreads();
+    }
+  }
+  if (pool && tid < d) {
+    const float mean = __fdiv_rn(acc, (float)nv);
+    (which == 0 ? qbar : kbar)[((size_t)h * g.nb + b) * d + tid] = mean;
+    if (which == 1) kbarT[((size_t)h * d + tid) * g.nb + b] = mean;
   }
 }
 
@@ -209,39 +224,56 @@ __global__ __launch_bounds__(256) void draft_select_kernel(const float* __restri
   }
   __syncthreads();
 
+  // A row's codes are read in groups of 16 per lane (code m of a group is
+  // block 64 (g0 + m) + lane); a row of at most 1024 blocks stays in
+  // registers for the whole selection, longer rows are re-read from LDS on
+  // every pass. Pads hold code 0, which neither a bisection candidate (>= 1)
+  // nor a "> tau" test counts; the final pass skips them explicitly.
   const int w = tid >> 6, lane = tid & 63;
   const int nch = nb64 >> 6;
+  const bool resident = nch <= 16;
   for (int r = w; r < nr; r += (int)(blockDim.x >> 6)) {
     const unsigned int* row = codes + r * nb64;
+    unsigned int a[16];
+    auto load_group = [&](int g0) {
+#pragma unroll
+      for (int m = 0; m < 16; ++m) a[m] = g0 + m < nch ? row[64 * (g0 + m) + lane] : 0u;
+    };
+    if (resident) load_group(0);
     unsigned int tau = 0u;
     for (int bit = 31; bit >= 0; --bit) {
       const unsigned int cand = tau | (1u << bit);
       int cnt = 0;
-      for (int m = 0; m < nch; ++m) {
-        const int j = 64 * m + lane;
-        cnt += __popcll(__ballot(j < nb && row[j] >= cand));
+      for (int g0 = 0; g0 < nch; g0 += 16) {
+        if (!resident) load_group(g0);
+#pragma unroll
+        for (int m = 0; m < 16; ++m) cnt += __popcll(__ballot(a[m] >= cand));
       }
       if (cnt >= topk) tau = cand;
     }
     int greater = 0;
-    for (int m = 0; m < nch; ++m) {
-      const int j = 64 * m + lane;
-      greater += __popcll(__ballot(j < nb && row[j] > tau));
+    for (int g0 = 0; g0 < nch; g0 += 16) {
+      if (!resident) load_group(g0);
+#pragma unroll
+      for (int m = 0; m < 16; ++m) greater += __popcll(__ballot(a[m] > tau));
     }
     const int need_eq = topk - greater;
     int32_t* out = kv_idx + ((size_t)h * nb + i0 + r) * topk;
     int eq_seen = 0, base = 0;
-    for (int m = 0; m < nch; ++m) {
-      const int j = 64 * m + lane;
-      const bool valid = j < nb;
-      const unsigned int a = row[j];
-      const bool eq = valid && a == tau;
-      const unsigned long long eqm = __ballot(eq);
-      const bool take = valid && (a > tau || (eq && eq_seen + lanes_below(eqm) < need_eq));
-      const unsigned long long tm = __ballot(take);
-      if (take) out[base + lanes_below(tm)] = j;
-      eq_seen += __popcll(eqm);
-      base += __popcll(tm);
+    for (int g0 = 0; g0 < nch; g0 += 16) {
+      if (!resident) load_group(g0);
+#pragma unroll
+      for (int m = 0; m < 16; ++m) {
+        const int j = 64 * (g0 + m) + lane;
+        const bool ok = j < nb;
+        const bool eq = ok && a[m] == tau;
+        const unsigned long long eqm = __ballot(eq);
+        const bool take = ok && (a[m] > tau || (eq && eq_seen + lanes_below(eqm) < need_eq));
+        const unsigned long long tm = __ballot(take);
+        if (take) out[base + lanes_below(tm)] = j;
+        eq_seen += __popcll(eqm);
+        base += __popcll(tm);
+      }
     }
     if (lane == 0) kv_cnt[(size_t)h * nb + i0 + r] = topk;
   }
@@ -261,22 +293,33 @@ __global__ void draft_scores_kernel(const float* __restrict__ qbar, const float*
 }
 
 // ---------------------------------------------------------------------------
-// Row gather with zero fill: one 16-byte chunk per thread, grid-stride.
+// Row gather with zero fill. A workgroup moves 1024 consecutive 16-byte
+// chunks of one head's destination (4 per thread, 256 apart, so every load
+// and store instruction of a wave touches 1 KB of consecutive bytes).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void token_permute_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
-                                                            int heads, int n_src, int n_dst, int cpr,
+                                                            int n_src, int n_dst, int cpr, int wg_per_head,
                                                             const int32_t* __restrict__ map) {
-  const size_t total = (size_t)heads * n_dst * cpr;
-  const size_t stride = (size_t)gridDim.x * blockDim.x;
-  for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += stride) {
-    const size_t row = e / cpr;
-    const int ch = (int)(e - row * cpr);
-    const int h = (int)(row / n_dst);
-    const int i = (int)(row - (size_t)h * n_dst);
-    const int s = map[i];
-    u32x4 x = {0u, 0u, 0u, 0u};
-    if (s >= 0 && s < n_src) x = src[((size_t)h * n_src + s) * cpr + ch];
-    dst[e] = x;
+  const int h = blockIdx.x / wg_per_head;
+  const int e0 = (blockIdx.x - h * wg_per_head) * 1024 + threadIdx.x;
+  const int total = n_dst * cpr;
+  const u32x4* S = src + (size_t)h * n_src * cpr;
+  u32x4* D = dst + (size_t)h * n_dst * cpr;
+  u32x4 x[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = e0 + 256 * i;
+    x[i] = u32x4{0u, 0u, 0u, 0u};
+    if (e < total) {
+      const int row = e / cpr, ch = e - row * cpr;
+      const int s = map[row];
+      if (s >= 0 && s < n_src) x[i] = S[(size_t)s * cpr + ch];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = e0 + 256 * i;
+    if (e < total) D[e] = x[i];
   }
 }
 
@@ -292,11 +335,8 @@ hipError_t launch_draft_perm(const DraftGeom& g, int32_t* perm, int32_t* inv_per
 hipError_t launch_draft_pool_gather(const DraftGeom& g, int heads, int d, int dt, const void* q, const void* k,
                                     const void* v, float* qbar, float* kbar, float* kbarT, void* q_perm,
                                     void* k_perm, void* v_perm, hipStream_t s) {
-  const int ch = dt == 1 ? 8 : 4;
-  const int lpr = d / ch;
-  const int gpb = 256 / lpr;
-  const int groups = heads * g.nb;
-  dim3 grid((groups + gpb - 1) / gpb, v_perm ? 3 : 2), block(256);
+  const int items = (v_perm ? 3 : 2) * heads * g.nb;
+  dim3 grid(items), block(256);
   if (dt == 1)
     hipLaunchKernelGGL(draft_pool_gather_kernel<true>, grid, block, 0, s, g, heads, d, q, k, v, qbar, kbar, kbarT,
                        q_perm, k_perm, v_perm);
@@ -310,7 +350,7 @@ hipError_t launch_draft_select(const float* qbar, const float* kbarT, int heads,
                                int32_t* kv_idx, int32_t* kv_cnt, hipStream_t s) {
   // Rows per workgroup so that the score codes take at most 32 KB of LDS.
   const int nb64 = (nb + 63) & ~63;
-  const int R = nb64 <= 1024 ? 8 : (nb64 <= 2048 ? 4 : 2);
+  const int R = nb64 <= 1024 ? 8 : (nb64 <= 2048 ? 4 : 2);  // R * nb64 <= 8192
   const size_t shm = (size_t)R * nb64 * sizeof(unsigned int);
   dim3 grid(heads * ((nb + R - 1) / R)), block(256);
   if (R == 8)
@@ -332,12 +372,10 @@ hipError_t launch_draft_scores(const float* qbar, const float* kbar, int heads, 
 hipError_t launch_token_permute(const void* src, void* dst, int esize, int heads, int n_src, int n_dst, int d,
                                 const int32_t* map, hipStream_t s) {
   const int cpr = d * esize / 16;
-  const size_t total = (size_t)heads * n_dst * cpr;
-  if (total == 0) return hipSuccess;
-  size_t blocks = (total + 255) / 256;
-  if (blocks > 65536) blocks = 65536;
-  hipLaunchKernelGGL(token_permute_kernel, dim3((unsigned)blocks), dim3(256), 0, s, (const u32x4*)src, (u32x4*)dst,
-                     heads, n_src, n_dst, cpr, map);
+  const long long per_head = ((long long)n_dst * cpr + 1023) / 1024;
+  if ((long long)heads * per_head == 0) return hipSuccess;
+  hipLaunchKernelGGL(token_permute_kernel, dim3((unsigned)(heads * per_head)), dim3(256), 0, s, (const u32x4*)src,
+                     (u32x4*)dst, n_src, n_dst, cpr, (int)per_head, map);
   return hipGetLastError();
 }
 
