@@ -518,7 +518,11 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
 
-template <int MODE>
+// SKIP: waves whose 32 rows hold no valid query (pad slots of reordered
+// blocks) skip the math but still take their share of the loads and every
+// barrier. Only instantiated for launches with per-block valid counts: the
+// extra branch splits the loop body and costs the list walk some overlap.
+template <int MODE, bool SKIP>
 __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_d128_kernel(AttnArgs a) {
   constexpr int D = 128, BN = 64, KSTEPS = 8, NKB = 2, PVSTEPS = 4, NDB = 4;
   constexpr int TILE = BN * D * 2;  // 16 KB per K or V tile
@@ -557,6 +561,7 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_d128_kernel(AttnArgs a) {
   const int qend = min(blk_lo + qlim, blk_end);
   const int row_lo = blk_lo + qt * kBM;
   const int qrow = row_lo + wave * 32 + l32;
+  const bool active = !SKIP || row_lo + wave * 32 < qend;
   const bool q_in_blk = qrow < blk_end;
   const bool q_valid = qrow < qend;
 
@@ -685,7 +690,7 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_d128_kernel(AttnArgs a) {
   }
   wait_dma();
   __syncthreads();
-  if (ntiles > 0) qk(0, s);
+  if (ntiles > 0 && active) qk(0, s);
   __syncthreads();
 
   auto step = [&](const int st, f32x16 (&cur)[NKB], f32x16 (&nxt)[NKB]) {
@@ -698,64 +703,67 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_d128_kernel(AttnArgs a) {
     load_k(tk, st);
     load_v(tv, st ^ 1);
 
-    if (!full_cur) {
+    if (active) {
+      if (!full_cur) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const unsigned f4 = kval[st][(kb * 32 + 8 * g + 4 * half) >> 2];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (((f4 >> (8 * i)) & 0xffu) == 0u) cur[kb][4 * g + i] = -INFINITY;
+          }
+      }
+
+      qk(st ^ 1, nxt);
+
+      float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const unsigned f4 = kval[st][(kb * 32 + 8 * g + 4 * half) >> 2];
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, cur[kb][r]);
+      mx = half_max(mx) * c;
+      const bool need = mx > mc + kRescale;
+      const float mc_new = need ? mx : mc;
+      const float alpha = need ? __builtin_amdgcn_exp2f(mc - mc_new) : 1.f;
+      mc = mc_new;
+      l_run *= alpha;
+      const float nm = (mc == -INFINITY) ? 0.f : -mc;
+
+      bf16x8 pb[PVSTEPS];
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (((f4 >> (8 * i)) & 0xffu) == 0u) cur[kb][4 * g + i] = -INFINITY;
+      for (int kk = 0; kk < PVSTEPS; ++kk) {
+#pragma unroll
+        for (int j = 0; j < 8; j += 2) {
+          const float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(cur[kk >> 1][8 * (kk & 1) + j], c, nm));
+          const float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(cur[kk >> 1][8 * (kk & 1) + j + 1], c, nm));
+          const bf16x2 p2 = {(__bf16)x0, (__bf16)x1};
+          l_run = __builtin_amdgcn_fdot2_f32_bf16(p2, ones, l_run, false);
+          pb[kk][j] = p2[0];
+          pb[kk][j + 1] = p2[1];
         }
-    }
-
-    qk(st ^ 1, nxt);
-
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, cur[kb][r]);
-    mx = half_max(mx) * c;
-    const bool need = mx > mc + kRescale;
-    const float mc_new = need ? mx : mc;
-    const float alpha = need ? __builtin_amdgcn_exp2f(mc - mc_new) : 1.f;
-    mc = mc_new;
-    l_run *= alpha;
-    const float nm = (mc == -INFINITY) ? 0.f : -mc;
-
-    bf16x8 pb[PVSTEPS];
-#pragma unroll
-    for (int kk = 0; kk < PVSTEPS; ++kk) {
-#pragma unroll
-      for (int j = 0; j < 8; j += 2) {
-        const float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(cur[kk >> 1][8 * (kk & 1) + j], c, nm));
-        const float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(cur[kk >> 1][8 * (kk & 1) + j + 1], c, nm));
-        const bf16x2 p2 = {(__bf16)x0, (__bf16)x1};
-        l_run = __builtin_amdgcn_fdot2_f32_bf16(p2, ones, l_run, false);
-        pb[kk][j] = p2[0];
-        pb[kk][j + 1] = p2[1];
       }
-    }
 
-    if (__ballot(need && (l_run == l_run)) != 0ull) {
+      if (__ballot(need && (l_run == l_run)) != 0ull) {
 #pragma unroll
-      for (int i = 0; i < NDB; ++i)
+        for (int i = 0; i < NDB; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
-    }
-
-#pragma unroll
-    for (int kk = 0; kk < PVSTEPS; ++kk) {
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        lds_u8* const vb = (lds_u8*)vbuf(st) + vra[db] + 16 * kk * 256;
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)vb);
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + 8 * 256));
-        const s16x4 both[2] = {lo, hi};
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, both), pb[kk], oacc[db], 0, 0, 0);
+          for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
       }
+
+#pragma unroll
+      for (int kk = 0; kk < PVSTEPS; ++kk) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          lds_u8* const vb = (lds_u8*)vbuf(st) + vra[db] + 16 * kk * 256;
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)vb);
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + 8 * 256));
+          const s16x4 both[2] = {lo, hi};
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, both), pb[kk], oacc[db], 0, 0, 0);
+        }
+      }
+
     }
 
     full_cur = tv.full;
@@ -808,11 +816,13 @@ hipError_t launch_mode(const AttnArgs& a, hipStream_t s) {
 hipError_t launch_d128(const AttnArgs& a, hipStream_t s) {
   dim3 grid(a.total_tiles), block(kThreads);
   if (a.dense)
-    hipLaunchKernelGGL(bsa_fwd_d128_kernel<MODE_DENSE>, grid, block, 0, s, a);
+    hipLaunchKernelGGL((bsa_fwd_d128_kernel<MODE_DENSE, false>), grid, block, 0, s, a);
+  else if (a.block_k >= 64 && a.block_valid)
+    hipLaunchKernelGGL((bsa_fwd_d128_kernel<MODE_LIST, true>), grid, block, 0, s, a);
   else if (a.block_k >= 64)
-    hipLaunchKernelGGL(bsa_fwd_d128_kernel<MODE_LIST>, grid, block, 0, s, a);
+    hipLaunchKernelGGL((bsa_fwd_d128_kernel<MODE_LIST, false>), grid, block, 0, s, a);
   else
-    hipLaunchKernelGGL(bsa_fwd_d128_kernel<MODE_SMALL>, grid, block, 0, s, a);
+    hipLaunchKernelGGL((bsa_fwd_d128_kernel<MODE_SMALL, false>), grid, block, 0, s, a);
   return hipGetLastError();
 }
 
