@@ -221,7 +221,7 @@ def run_lvsa(args, w):
         "unit": "TFLOP/s",
         "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
         "traffic": traffic_for(w.name, ATTN_SRC),
-        "kernel": "bsa_fwd_d128_kernel<MODE_LIST>",
+        "kernel": "bsa_fwd_d128_kernel<MODE_LIST, false>",
     }
 
     if not args.no_dense:
@@ -320,7 +320,7 @@ def run_draft(args, w):
         "roofline": {"bound": "mfma", "achieved": round(flops / (attn_avg * 1e-3) / 1e12, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(flops / (attn_avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic_for(w.name, ATTN_SRC), "kernel": "bsa_fwd_d128_kernel<MODE_LIST>"},
+                     "traffic": traffic_for(w.name, ATTN_SRC), "kernel": "bsa_fwd_d128_kernel<MODE_LIST, true>"},
     }
     return res
 

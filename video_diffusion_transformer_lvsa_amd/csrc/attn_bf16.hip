@@ -12,17 +12,20 @@
 //    list slot i covers virtual rows [i*block_k, (i+1)*block_k). Tiles of
 //    BN virtual rows are gathered row by row, so a frame list of 21 frames
 //    of 1560 tokens is 512 tiles of 64 with only the last one ragged,
-//    whatever the frame size. Rows are fetched with buffer loads; a row
-//    that is not a valid key gets an offset past the end of the buffer and
-//    reads as zero.
+//    whatever the frame size. A row that is not a valid key gets a buffer
+//    offset past the end of the buffer and reads as zero.
 //  * Scores are formed transposed, Sᵀ = K Qᵀ, with v_mfma_f32_32x32x16_bf16:
 //    the accumulator layout gives each lane one query column and 16 keys
 //    per 32x32 block, so the row max/sum of the online softmax is in-lane
 //    work plus one v_permlane32_swap between the half-waves, and Pᵀ is
 //    already in the B-operand layout of the second product Oᵀ += Vᵀ Pᵀ.
-//  * Q stays in VGPRs for the whole key walk. K is staged row-major in LDS,
-//    V transposed (Vᵀ, keys contiguous) by an in-register 4x8 transpose;
-//    both use XOR swizzles instead of padding.
+//  * Q stays in VGPRs for the whole key walk.
+//  * d = 128 (bsa_fwd_d128_kernel): K and V tiles go from global memory
+//    straight into LDS with buffer loads that have an LDS destination; Vᵀ
+//    operands are read from the row-major V tile with ds_read_b64_tr_b16.
+//    d = 64 (bsa_fwd_bf16_kernel): rows are staged through VGPRs and V is
+//    transposed in registers (4x8) before it is written to LDS. Both use
+//    XOR swizzles instead of padding.
 //  * Software pipeline, one barrier per tile: while the softmax of tile i
 //    runs on the VALU, the MFMAs of Sᵀ for tile i+1 run on the matrix core
 //    (K runs one tile ahead of V in LDS, two tiles ahead in global loads).
