@@ -264,9 +264,11 @@ def run_draft(args, w):
     dq, dk, dv = up(q), up(k), up(v)
     bs = w.pool_h * w.pool_w
     stream = torch.cuda.current_stream()
+    sparsity = w.sparsity if args.sparsity is None else args.sparsity
+    pool = args.pool
 
     def step():
-        out = _lib.draft_mask_and_perm(dq, dk, dv, w.T, w.H, w.W, w.pool_h, w.pool_w, w.sparsity)
+        out = _lib.draft_mask_and_perm(dq, dk, dv, w.T, w.H, w.W, w.pool_h, w.pool_w, sparsity, pool=pool)
         op = _lib.block_sparse_attn_fwd(out["q_perm"], out["k_perm"], out["v_perm"], bs, bs, out["kv_idx"],
                                         out["kv_cnt"], mask_heads=w.heads, block_valid=out["block_valid"])
         o = _lib.token_permute(op, out["inv_perm"])
@@ -285,7 +287,7 @@ def run_draft(args, w):
     t0.record(stream)
     for _ in range(args.steps):
         e[0].record(stream)
-        out = _lib.draft_mask_and_perm(dq, dk, dv, w.T, w.H, w.W, w.pool_h, w.pool_w, w.sparsity)
+        out = _lib.draft_mask_and_perm(dq, dk, dv, w.T, w.H, w.W, w.pool_h, w.pool_w, sparsity, pool=pool)
         e[1].record(stream)
         op = _lib.block_sparse_attn_fwd(out["q_perm"], out["k_perm"], out["v_perm"], bs, bs, out["kv_idx"],
                                         out["kv_cnt"], mask_heads=w.heads, block_valid=out["block_valid"])
@@ -314,8 +316,9 @@ def run_draft(args, w):
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": WORKLOAD_NAMES[w.name], "T": w.T, "H": w.H, "W": w.W, "heads": w.heads, "d": w.d,
-                   "pool": [w.pool_h, w.pool_w], "sparsity": w.sparsity, "flop_per_call": flops},
+        "config": {"workload": f"hunyuanvideo-draft-{round(100 * sparsity)}pct" + ("-maxpool" if pool == "max" else ""),
+                   "T": w.T, "H": w.H, "W": w.W, "heads": w.heads, "d": w.d, "pool": [w.pool_h, w.pool_w],
+                   "pooling": pool, "sparsity": sparsity, "top_k": int(kv.shape[-1]), "flop_per_call": flops},
         "stage_ms": {k2: round(sum(v2) / len(v2), 4) for k2, v2 in times.items()},
         "roofline": {"bound": "mfma", "achieved": round(flops / (attn_avg * 1e-3) / 1e12, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
@@ -334,6 +337,8 @@ def main(argv=None) -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--sparsity", type=float, default=None, help="Draft workload: override the 90%% sparsity")
+    ap.add_argument("--pool", choices=("mean", "max"), default="mean", help="Draft workload: pooling of Q and K")
     ap.add_argument("--dense-steps", type=int, default=3)
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="first run a plain row copy (token_permute, identity map) over this many MiB, 3 times, "

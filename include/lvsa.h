@@ -57,6 +57,10 @@ typedef enum {
 
 typedef enum { LVSA_F32 = 0, LVSA_BF16 = 1 } lvsa_dtype;
 
+/* Draft pooling of Q and K: the mean (the article's choice) or the maximum
+ * (the variant it compares against). */
+typedef enum { LVSA_POOL_MEAN = 0, LVSA_POOL_MAX = 1 } lvsa_pool;
+
 /* Text of the calling thread's last failure ("" if none). Host pointer owned
  * by the library, valid until the thread's next call. */
 const char* lvsa_last_error(void);
@@ -103,7 +107,9 @@ int lvsa_mask(int T, int C, int window, int T_per, int step, int32_t* kv_idx, in
  *   block_valid[b] number of valid tokens of block b (they are its first slots).
  * Pooling: for each head, block and channel c, acc = +0.0f, then acc += x for
  *   each valid token in slot order (each add rounded to fp32), mean = acc/count
- *   (one IEEE fp32 division). Applied to Q and to K.
+ *   (one IEEE fp32 division). Applied to Q and to K. With LVSA_POOL_MAX the
+ *   pooled value is the largest x over the valid tokens, plus +0.0f (so a
+ *   zero result is +0); Q and K must then be finite.
  * Draft map: s[h,i,j] = fold over c = 0..d-1 of acc = fl(acc + fl(q̄[i,c]*k̄[j,c]))
  *   starting from +0.0f, no fused multiply-add (the unscaled logit: softmax and
  *   1/sqrt(d) do not change a row's ranking).
@@ -125,6 +131,7 @@ size_t draft_workspace_bytes(int heads, int T, int H, int grid_w, int d, int poo
 
 /* Full Draft mask builder on Q, K (and the reorder of Q, K, V).
  *   q, k, v     [heads, T*H*grid_w, d] of dtype dt (v may be NULL when v_perm is NULL)
+ *   pool_mode   LVSA_POOL_MEAN or LVSA_POOL_MAX (LVSA_EINVAL otherwise)
  *   kv_idx      out [heads, nb, k] int32 (k from draft_grid_info)
  *   kv_cnt      out [heads, nb] int32 (= k)
  *   perm        out [N_pad] int32; inv_perm out [T*H*grid_w] int32; block_valid out [nb] int32
@@ -134,7 +141,7 @@ size_t draft_workspace_bytes(int heads, int T, int H, int grid_w, int d, int poo
  *               holds Q̄, K̄ and K̄ᵀ on return (layout above).
  * Requires block size <= 1024 and nb <= 4096. */
 int draft_mask_and_perm(const void* q, const void* k, const void* v, int dt, int heads, int T, int H, int grid_w,
-                        int d, int pool_h, int pool_w, double sparsity, int32_t* kv_idx, int32_t* kv_cnt,
+                        int d, int pool_h, int pool_w, double sparsity, int pool_mode, int32_t* kv_idx, int32_t* kv_cnt,
                         int32_t* perm, int32_t* inv_perm, int32_t* block_valid, void* q_perm, void* k_perm,
                         void* v_perm, void* workspace, size_t ws_bytes, void* stream);
 

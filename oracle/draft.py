@@ -14,7 +14,8 @@ Source: "ç§‘å­¦å®¶æå‡ºè§†é¢‘æ‰©æ•£æ¨¡å‹åŠ é€Ÿæ–¹æ³•ï¼Œåœ¨H100å®ç°ä¸€å€ä»¥ä
 * a reorder gathers the scattered sparse blocks into a contiguous layout
   (the "Full Map" -> "Reordered Full Map" figure paragraph);
 * average pooling beats max pooling at high sparsity, and the method is run
-  at 90% sparsity (paragraphs on the design details and the experiments).
+  at 90% sparsity (paragraphs on the design details and the experiments);
+  both poolings are provided.
 
 Readings taken where the article leaves a step open (every one is listed in
 the design notes of the repository):
@@ -117,16 +118,29 @@ def draft_permutation(g: DraftGrid):
     return perm, inv_perm, block_valid
 
 
-def draft_pool(x: np.ndarray, g: DraftGrid) -> np.ndarray:
-    """Per-tile fp32 mean of x ([heads, N, d], fp32 values) over valid tokens.
+def draft_pool(x: np.ndarray, g: DraftGrid, mode: str = "mean") -> np.ndarray:
+    """Per-tile fp32 mean (or maximum) of x ([heads, N, d], fp32 values) over valid tokens.
 
-    acc starts at +0.0; the tile's valid tokens are added one at a time in
-    slot order, each add rounded to fp32; the mean is one fp32 division."""
+    mean: acc starts at +0.0; the tile's valid tokens are added one at a time
+    in slot order, each add rounded to fp32; the mean is one fp32 division.
+    max: the largest value over the valid tokens, plus +0.0 (a zero result is
+    +0); exact, so the order does not matter."""
     x = np.asarray(x, dtype=np.float32)
     heads, n, d = x.shape
     assert n == g.N
     perm, _, block_valid = draft_permutation(g)
     bs = g.block_size
+    if mode == "max":
+        if not np.all(np.isfinite(x)):
+            raise ValueError("max pooling needs finite inputs")
+        out = np.full((heads, g.nb, d), -np.inf, dtype=np.float32)
+        pb = perm.reshape(g.nb, bs)
+        for b in range(g.nb):
+            rows = pb[b, : block_valid[b]]
+            out[:, b, :] = x[:, rows, :].max(axis=1)
+        return (out + np.float32(0.0)).astype(np.float32)
+    if mode != "mean":
+        raise ValueError(f"unknown pooling {mode!r}")
     acc = np.zeros((heads, g.nb, d), dtype=np.float32)
     pb = perm.reshape(g.nb, bs)
     for slot in range(bs):
@@ -176,12 +190,12 @@ def draft_topk(scores: np.ndarray, k: int) -> np.ndarray:
     return out
 
 
-def draft_mask(q: np.ndarray, k: np.ndarray, g: DraftGrid, sparsity: float):
+def draft_mask(q: np.ndarray, k: np.ndarray, g: DraftGrid, sparsity: float, pool: str = "mean"):
     """Full Draft mask builder on fp32 inputs [heads, N, d].
 
     Returns (kv_idx [heads, nb, k], kv_cnt [heads, nb], qbar, kbar, scores)."""
-    qbar = draft_pool(q, g)
-    kbar = draft_pool(k, g)
+    qbar = draft_pool(q, g, pool)
+    kbar = draft_pool(k, g, pool)
     s = draft_scores(qbar, kbar)
     kk = topk_count(sparsity, g.nb)
     kv_idx = draft_topk(s, kk)

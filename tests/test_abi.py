@@ -117,11 +117,15 @@ def test_mask_and_permute_validation(lib):
     assert tp(FAKE, FAKE, 1, 2, 10, 0, 128, FAKE, None) == 0
     assert tp(FAKE, FAKE, 1, 2, 1 << 27, 10, 128, FAKE, None) == _lib.LVSA_EINVAL  # 2^31 chunks per head
     dm = lib.draft_mask_and_perm
-    base = [FAKE, FAKE, FAKE, 1, 2, 2, 10, 16, 128, 4, 8, 0.5, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE]
+    base = [FAKE, FAKE, FAKE, 1, 2, 2, 10, 16, 128, 4, 8, 0.5, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE]
     need = lib.draft_workspace_bytes(2, 2, 10, 16, 128, 4, 8)
     assert dm(*base, FAKE, need - 4, None) == _lib.LVSA_ENOMEM
     bad = list(base)
-    bad[18] = None  # k_perm NULL but q_perm set
+    bad[12] = 2  # pool mode
+    assert dm(*bad, FAKE, need, None) == _lib.LVSA_EINVAL
+    assert "pool_mode" in _lib.last_error()
+    bad = list(base)
+    bad[19] = None  # k_perm NULL but q_perm set
     assert dm(*bad, FAKE, need, None) == _lib.LVSA_EINVAL
     bad = list(base)
     bad[8] = 80

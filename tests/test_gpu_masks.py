@@ -58,16 +58,16 @@ def _inputs(T, H, W, heads, d, dtype, seed):
     return q, k, v, synth.bf16_to_f32(q), synth.bf16_to_f32(k)
 
 
-def _check_draft(T, H, W, ph, pw, heads, d, sp, dtype, seed):
+def _check_draft(T, H, W, ph, pw, heads, d, sp, dtype, seed, pool="mean"):
     q, k, v, qf, kf = _inputs(T, H, W, heads, d, dtype, seed)
-    note(f"draft_mask_and_perm T={T} H={H} W={W} pool={ph}x{pw} heads={heads} d={d} sparsity={sp} {dtype}")
-    out = _lib.draft_mask_and_perm(to_dev(q), to_dev(k), to_dev(v), T, H, W, ph, pw, sp)
+    note(f"draft_mask_and_perm T={T} H={H} W={W} pool={ph}x{pw} {pool} heads={heads} d={d} sparsity={sp} {dtype}")
+    out = _lib.draft_mask_and_perm(to_dev(q), to_dev(k), to_dev(v), T, H, W, ph, pw, sp, pool=pool)
     g = oracle.draft_grid(T, H, W, ph, pw)
     perm, inv, bv = oracle.draft_permutation(g)
     assert np.array_equal(to_host(out["perm"]), perm)
     assert np.array_equal(to_host(out["inv_perm"]), inv)
     assert np.array_equal(to_host(out["block_valid"]), bv)
-    qbar, kbar = oracle.draft_pool(qf, g), oracle.draft_pool(kf, g)
+    qbar, kbar = oracle.draft_pool(qf, g, pool), oracle.draft_pool(kf, g, pool)
     assert np.array_equal(to_host(out["qbar"]).view(np.uint32), qbar.view(np.uint32))
     assert np.array_equal(to_host(out["kbar"]).view(np.uint32), kbar.view(np.uint32))
     s = oracle.draft_scores(qbar, kbar)
@@ -88,6 +88,16 @@ def _check_draft(T, H, W, ph, pw, heads, d, sp, dtype, seed):
 @pytest.mark.parametrize("case", DRAFT_CASES)
 def test_draft_bit_exact(case):
     _check_draft(*case, seed=21)
+
+
+@pytest.mark.parametrize("case", [DRAFT_CASES[i] for i in (0, 1, 3, 5)])
+def test_draft_max_pool_bit_exact(case):
+    _check_draft(*case, seed=22, pool="max")
+
+
+def test_draft_hunyuan_full_size_max_pool_bit_exact():
+    w = synth.WORKLOADS["hunyuan-draft"]
+    _check_draft(w.T, w.H, w.W, w.pool_h, w.pool_w, w.heads, w.d, w.sparsity, "bf16", seed=w.seed, pool="max")
 
 
 def test_draft_hunyuan_full_size_bit_exact():

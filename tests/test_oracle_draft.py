@@ -101,6 +101,59 @@ def test_pool_constant_tile():
             assert np.allclose(got[0, b], blk_val[b], rtol=4e-7)
 
 
+def _max_pool_brute(x, g):
+    """Per tile and channel, the largest value over the tile's valid tokens,
+    walking the padded [t, y, x] grid directly with Python loops."""
+    heads, _, d = x.shape
+    out = np.zeros((heads, g.nb, d), dtype=np.float32)
+    b = 0
+    for t in range(g.T):
+        for hb in range(g.nbh):
+            for wb in range(g.nbw):
+                for h in range(heads):
+                    for c in range(d):
+                        best = None
+                        for yy in range(hb * g.pool_h, min((hb + 1) * g.pool_h, g.H)):
+                            for xx in range(wb * g.pool_w, min((wb + 1) * g.pool_w, g.W)):
+                                v = float(x[h, (t * g.H + yy) * g.W + xx, c])
+                                best = v if best is None or v > best else best
+                        out[h, b, c] = np.float32(best) + np.float32(0.0)
+                b += 1
+    return out
+
+
+@pytest.mark.parametrize("T,H,W,ph,pw", [(2, 5, 7, 2, 4), (1, 9, 10, 4, 8)])
+def test_max_pool_brute_force(T, H, W, ph, pw):
+    g = oracle.draft_grid(T, H, W, ph, pw)
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((2, g.N, 3)).astype(np.float32)
+    assert np.array_equal(oracle.draft_pool(x, g, "max"), _max_pool_brute(x, g))
+
+
+def test_max_pool_excludes_pads_and_folds_negative_zero():
+    # All values negative on a grid with ragged tiles: a pad counted as 0 would win.
+    g = oracle.draft_grid(2, 5, 7, 2, 4)
+    rng = np.random.default_rng(6)
+    x = -np.abs(rng.standard_normal((1, g.N, 4))).astype(np.float32) - np.float32(0.5)
+    got = oracle.draft_pool(x, g, "max")
+    assert np.all(got < 0)
+    assert np.array_equal(got, _max_pool_brute(x, g))
+    z = np.full((1, g.N, 2), -0.0, dtype=np.float32)
+    zp = oracle.draft_pool(z, g, "max")
+    assert np.all(zp == 0) and not np.any(np.signbit(zp))
+
+
+def test_max_pool_bounds_mean():
+    g = oracle.draft_grid(3, 12, 20, 8, 16)
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal((2, g.N, 4)).astype(np.float32)
+    mx = oracle.draft_pool(x, g, "max")
+    mean = oracle.draft_pool(x, g, "mean")
+    assert np.all(mx >= mean)
+    with pytest.raises(ValueError):
+        oracle.draft_pool(x, g, "median")
+
+
 def test_scores_exact_on_integers():
     rng = np.random.default_rng(2)
     q = rng.integers(-30, 30, size=(2, 9, 16)).astype(np.float32)

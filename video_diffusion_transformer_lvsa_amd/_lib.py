@@ -29,7 +29,7 @@ SIGNATURES = {
     "lvsa_mask": (_c_int, [_c_int] * 5 + [_p, _p, _c_int, _p]),
     "draft_grid_info": (_c_int, [_c_int] * 5 + [_c_dbl, _pint, _pint, _pint, _pint]),
     "draft_workspace_bytes": (_c_sz, [_c_int] * 7),
-    "draft_mask_and_perm": (_c_int, [_p, _p, _p] + [_c_int] * 8 + [_c_dbl] + [_p] * 9 + [_c_sz, _p]),
+    "draft_mask_and_perm": (_c_int, [_p, _p, _p] + [_c_int] * 8 + [_c_dbl, _c_int] + [_p] * 9 + [_c_sz, _p]),
     "draft_scores": (_c_int, [_p, _p] + [_c_int] * 4 + [_p, _p]),
     "token_permute": (_c_int, [_p, _p] + [_c_int] * 5 + [_p, _p]),
     "block_sparse_attn_fwd": (_c_int, [_p] * 4 + [_c_int] * 6 + [_p, _p, _c_int, _c_int, _p, _c_flt, _p]),
@@ -147,9 +147,13 @@ def draft_workspace_bytes(heads: int, T: int, H: int, grid_w: int, d: int, pool_
     return int(load().draft_workspace_bytes(heads, T, H, grid_w, d, pool_h, pool_w))
 
 
+POOL_MODES = {"mean": 0, "max": 1}
+
+
 def draft_mask_and_perm(q, k, v, T: int, H: int, grid_w: int, pool_h: int, pool_w: int, sparsity: float,
-                        reorder: bool = True, stream=None) -> dict:
-    """Draft mask builder + reorder. q, k, v: [heads, T*H*grid_w, d] on the GPU.
+                        reorder: bool = True, pool: str = "mean", stream=None) -> dict:
+    """Draft mask builder + reorder. q, k, v: [heads, T*H*grid_w, d] on the GPU;
+    pool is "mean" or "max".
 
     Returns a dict with kv_idx, kv_cnt, perm, inv_perm, block_valid, the
     reordered q_perm/k_perm/v_perm (if reorder) and qbar/kbar (views of the
@@ -175,7 +179,7 @@ def draft_mask_and_perm(q, k, v, T: int, H: int, grid_w: int, pool_h: int, pool_
     ws_bytes = draft_workspace_bytes(heads, T, H, grid_w, d, pool_h, pool_w)
     ws = torch.empty((ws_bytes // 4,), dtype=torch.float32, device=dev)
     _check(load().draft_mask_and_perm(
-        _ptr(q), _ptr(k), _ptr(v), _dt(q), heads, T, H, grid_w, d, pool_h, pool_w, sparsity,
+        _ptr(q), _ptr(k), _ptr(v), _dt(q), heads, T, H, grid_w, d, pool_h, pool_w, sparsity, POOL_MODES[pool],
         _ptr(out["kv_idx"]), _ptr(out["kv_cnt"]), _ptr(out["perm"]), _ptr(out["inv_perm"]), _ptr(out["block_valid"]),
         _ptr(out.get("q_perm")), _ptr(out.get("k_perm")), _ptr(out.get("v_perm")), _ptr(ws), ws_bytes,
         _stream(stream)))

@@ -221,13 +221,14 @@ size_t draft_workspace_bytes(int heads, int T, int H, int grid_w, int d, int poo
 }
 
 int draft_mask_and_perm(const void* q, const void* k, const void* v, int dt, int heads, int T, int H, int grid_w,
-                        int d, int pool_h, int pool_w, double sparsity, int32_t* kv_idx, int32_t* kv_cnt,
+                        int d, int pool_h, int pool_w, double sparsity, int pool_mode, int32_t* kv_idx, int32_t* kv_cnt,
                         int32_t* perm, int32_t* inv_perm, int32_t* block_valid, void* q_perm, void* k_perm,
                         void* v_perm, void* workspace, size_t ws_bytes, void* stream) {
   clear_err();
   if (dt != LVSA_F32 && dt != LVSA_BF16) return fail(LVSA_EINVAL, "dtype %d unknown", dt);
   if (d != 64 && d != 128) return fail(LVSA_EUNSUPPORTED, "head dim d=%d (supported: 64, 128)", d);
   if (heads < 1) return fail(LVSA_EINVAL, "heads=%d must be >= 1", heads);
+  if (pool_mode != LVSA_POOL_MEAN && pool_mode != LVSA_POOL_MAX) return fail(LVSA_EINVAL, "pool_mode %d unknown", pool_mode);
   lvsa::DraftGeom g;
   int rc = geom(T, H, grid_w, pool_h, pool_w, &g);
   if (rc) return rc;
@@ -255,8 +256,8 @@ int draft_mask_and_perm(const void* q, const void* k, const void* v, int dt, int
   float* kbarT = kbar + (size_t)heads * g.nb * d;
   rc = launched(lvsa::launch_draft_perm(g, perm, inv_perm, block_valid, s), "draft perm launch");
   if (rc) return rc;
-  rc = launched(lvsa::launch_draft_pool_gather(g, heads, d, dt, q, k, v, qbar, kbar, kbarT, q_perm, k_perm, v_perm,
-                                               s),
+  rc = launched(lvsa::launch_draft_pool_gather(g, heads, d, dt, pool_mode == LVSA_POOL_MAX, q, k, v, qbar, kbar, kbarT,
+                                               q_perm, k_perm, v_perm, s),
                 "draft pool launch");
   if (rc) return rc;
   return launched(lvsa::launch_draft_select(qbar, kbarT, heads, g.nb, d, topk, kv_idx, kv_cnt, s),

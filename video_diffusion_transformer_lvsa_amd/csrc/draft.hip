@@ -55,7 +55,8 @@ __global__ void draft_perm_kernel(DraftGeom g, int32_t* __restrict__ perm, int32
 // are contiguous in the source) and store them to the block's slots in the
 // reordered tensor, pads as zeros. For Q and K a stage is also staged in LDS,
 // where lane c folds channel c over the stage's slots in slot order, so every
-// channel's sum is one sequential fold across the whole block.
+// channel's sum is one sequential fold across the whole block (or, with
+// MAXP, its running maximum).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int xcd_local(int w, int G) {
   // Workgroup w runs on XCD w % 8: give each XCD a contiguous range of work
@@ -65,7 +66,7 @@ __device__ __forceinline__ int xcd_local(int w, int G) {
   return (xcd < r8 ? xcd * (q8 + 1) : r8 * (q8 + 1) + (xcd - r8) * q8) + idx;
 }
 
-template <bool BF16>
+template <bool BF16, bool MAXP>
 __global__ __launch_bounds__(256) void draft_pool_gather_kernel(DraftGeom g, int heads, int d,
                                                                 const void* __restrict__ q,
                                                                 const void* __restrict__ k,
@@ -102,7 +103,7 @@ __global__ __launch_bounds__(256) void draft_pool_gather_kernel(DraftGeom g, int
   const u32x4* S = (const u32x4*)src + (size_t)h * g.n * rowc;
   u32x4* Dd = dst ? (u32x4*)dst + ((size_t)h * g.n_pad + (size_t)b * g.bs) * rowc : nullptr;
 
-  float acc = 0.f;
+  float acc = MAXP ? -INFINITY : 0.f;
   for (int s0 = 0; s0 < g.bs; s0 += ROUNDS * rpr) {
     u32x4 x[ROUNDS];
 #pragma unroll
@@ -134,14 +135,14 @@ __global__ __launch_bounds__(256) void draft_pool_gather_kernel(DraftGeom g, int
             xv = __uint_as_float((unsigned int)*(const unsigned short*)(base + (size_t)r * d * ES) << 16);
           else
             xv = *(const float*)(base + (size_t)r * d * ES);
-          acc = __fadd_rn(acc, xv);
+          acc = MAXP ? fmaxf(acc, xv) : __fadd_rn(acc, xv);
         }
       }
       __syncthreads();
     }
   }
   if (pool && tid < d) {
-    const float mean = __fdiv_rn(acc, (float)nv);
+    const float mean = MAXP ? __fadd_rn(acc, 0.f) : __fdiv_rn(acc, (float)nv);
     (which == 0 ? qbar : kbar)[((size_t)h * g.nb + b) * d + tid] = mean;
     if (which == 1) kbarT[((size_t)h * d + tid) * g.nb + b] = mean;
   }
@@ -332,17 +333,19 @@ hipError_t launch_draft_perm(const DraftGeom& g, int32_t* perm, int32_t* inv_per
   return hipGetLastError();
 }
 
-hipError_t launch_draft_pool_gather(const DraftGeom& g, int heads, int d, int dt, const void* q, const void* k,
+hipError_t launch_draft_pool_gather(const DraftGeom& g, int heads, int d, int dt, bool pool_max, const void* q, const void* k,
                                     const void* v, float* qbar, float* kbar, float* kbarT, void* q_perm,
                                     void* k_perm, void* v_perm, hipStream_t s) {
   const int items = (v_perm ? 3 : 2) * heads * g.nb;
   dim3 grid(items), block(256);
-  if (dt == 1)
-    hipLaunchKernelGGL(draft_pool_gather_kernel<true>, grid, block, 0, s, g, heads, d, q, k, v, qbar, kbar, kbarT,
-                       q_perm, k_perm, v_perm);
-  else
-    hipLaunchKernelGGL(draft_pool_gather_kernel<false>, grid, block, 0, s, g, heads, d, q, k, v, qbar, kbar, kbarT,
-                       q_perm, k_perm, v_perm);
+#define LVSA_POOL_LAUNCH(BF, MX)                                                                              \
+  hipLaunchKernelGGL((draft_pool_gather_kernel<BF, MX>), grid, block, 0, s, g, heads, d, q, k, v, qbar, kbar, kbarT, \
+                     q_perm, k_perm, v_perm)
+  if (dt == 1 && pool_max) LVSA_POOL_LAUNCH(true, true);
+  else if (dt == 1) LVSA_POOL_LAUNCH(true, false);
+  else if (pool_max) LVSA_POOL_LAUNCH(false, true);
+  else LVSA_POOL_LAUNCH(false, false);
+#undef LVSA_POOL_LAUNCH
   return hipGetLastError();
 }
 

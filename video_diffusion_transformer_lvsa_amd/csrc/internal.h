@@ -52,9 +52,10 @@ struct DraftGeom {
 
 hipError_t launch_draft_perm(const DraftGeom& g, int32_t* perm, int32_t* inv_perm, int32_t* block_valid,
                              hipStream_t s);
-// Pools q and k (dtype 0 = f32, 1 = bf16) into qbar/kbar and, when the
-// *_perm pointers are non-NULL, writes the reordered tensors.
-hipError_t launch_draft_pool_gather(const DraftGeom& g, int heads, int d, int dt, const void* q, const void* k,
+// Pools q and k (dtype 0 = f32, 1 = bf16; mean, or maximum when pool_max)
+// into qbar/kbar and, when the *_perm pointers are non-NULL, writes the
+// reordered tensors.
+hipError_t launch_draft_pool_gather(const DraftGeom& g, int heads, int d, int dt, bool pool_max, const void* q, const void* k,
                                     const void* v, float* qbar, float* kbar, float* kbarT, void* q_perm,
                                     void* k_perm, void* v_perm, hipStream_t s);
 hipError_t launch_draft_select(const float* qbar, const float* kbarT, int heads, int nb, int d, int topk,
