@@ -39,6 +39,7 @@ WORKLOAD_NAMES = {
     "wan1.3b-1x": "wan2.1-1.3b-1x-lvsa-full",
     "wan14b-6x": "wan2.1-14b-6x-lvsa",
     "hunyuan-draft": "hunyuanvideo-draft-90pct",
+    "hunyuan-lvsa-2x": "hunyuanvideo-2x-lvsa",
 }
 
 

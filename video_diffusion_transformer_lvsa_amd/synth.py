@@ -160,8 +160,10 @@ class Workload:
 # The five workloads: a tiny CPU-checkable grid, Wan-2.1-1.3B at training
 # length (T = 21 latent frames of 30x52 tokens, 12 heads, d = 128) and at 6x
 # length (T = 126), HunyuanVideo-shaped Draft Attention (T = 33 frames of
-# 45x80 tokens, 24 heads, 8x16 pooling, 90% sparsity) and Wan-2.1-14B at 6x
-# length (40 heads).
+# 45x80 tokens, 24 heads, 8x16 pooling, 90% sparsity), Wan-2.1-14B at 6x
+# length (40 heads), and LVSA on a HunyuanVideo-shaped grid at 2x its
+# training length (257 video frames = 65 latent frames, budget C = 33 latent
+# frames = the 129-frame training length).
 WORKLOADS = {
     "tiny": Workload("tiny", T=4, H=8, W=8, heads=2, d=64, dtype="f32", kind="lvsa", seed=1,
                      C=3, window=2, T_per=2),
@@ -173,4 +175,6 @@ WORKLOADS = {
                               seed=4, pool_h=8, pool_w=16, sparsity=0.9),
     "wan14b-6x": Workload("wan14b-6x", T=126, H=30, W=52, heads=40, d=128, dtype="bf16", kind="lvsa",
                           seed=5, C=21, window=5, T_per=8),
+    "hunyuan-lvsa-2x": Workload("hunyuan-lvsa-2x", T=65, H=45, W=80, heads=24, d=128, dtype="bf16", kind="lvsa",
+                                seed=6, C=33, window=5, T_per=8),
 }
