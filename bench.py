@@ -268,11 +268,24 @@ def run_draft(args, w):
     sparsity = w.sparsity if args.sparsity is None else args.sparsity
     pool = args.pool
 
+    reorder = not args.no_reorder
+    o_raster = None if reorder else torch.empty((w.heads, w.N, w.d), dtype=torch.float32, device=dev)
+
+    def mask():
+        return _lib.draft_mask_and_perm(dq, dk, dv, w.T, w.H, w.W, w.pool_h, w.pool_w, sparsity, pool=pool,
+                                        reorder=reorder)
+
+    def attn(out):
+        if reorder:
+            return _lib.block_sparse_attn_fwd(out["q_perm"], out["k_perm"], out["v_perm"], bs, bs, out["kv_idx"],
+                                              out["kv_cnt"], mask_heads=w.heads, block_valid=out["block_valid"])
+        return _lib.draft_attn_fwd(dq, dk, dv, w.T, w.H, w.W, w.pool_h, w.pool_w, out["kv_idx"], out["kv_cnt"],
+                                   out=o_raster)
+
     def step():
-        out = _lib.draft_mask_and_perm(dq, dk, dv, w.T, w.H, w.W, w.pool_h, w.pool_w, sparsity, pool=pool)
-        op = _lib.block_sparse_attn_fwd(out["q_perm"], out["k_perm"], out["v_perm"], bs, bs, out["kv_idx"],
-                                        out["kv_cnt"], mask_heads=w.heads, block_valid=out["block_valid"])
-        o = _lib.token_permute(op, out["inv_perm"])
+        out = mask()
+        op = attn(out)
+        o = _lib.token_permute(op, out["inv_perm"]) if reorder else op
         return out, op, o
 
     for _ in range(args.warmup):
@@ -288,12 +301,12 @@ def run_draft(args, w):
     t0.record(stream)
     for _ in range(args.steps):
         e[0].record(stream)
-        out = _lib.draft_mask_and_perm(dq, dk, dv, w.T, w.H, w.W, w.pool_h, w.pool_w, sparsity, pool=pool)
+        out = mask()
         e[1].record(stream)
-        op = _lib.block_sparse_attn_fwd(out["q_perm"], out["k_perm"], out["v_perm"], bs, bs, out["kv_idx"],
-                                        out["kv_cnt"], mask_heads=w.heads, block_valid=out["block_valid"])
+        op = attn(out)
         e[2].record(stream)
-        _lib.token_permute(op, out["inv_perm"])
+        if reorder:
+            _lib.token_permute(op, out["inv_perm"])
         e[3].record(stream)
         torch.cuda.synchronize()
         times["mask"].append(e[0].elapsed_time(e[1]))
@@ -317,14 +330,16 @@ def run_draft(args, w):
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"hunyuanvideo-draft-{round(100 * sparsity)}pct" + ("-maxpool" if pool == "max" else ""),
+        "config": {"workload": f"hunyuanvideo-draft-{round(100 * sparsity)}pct" + ("-maxpool" if pool == "max" else "")
+                               + ("" if reorder else "-raster"),
                    "T": w.T, "H": w.H, "W": w.W, "heads": w.heads, "d": w.d, "pool": [w.pool_h, w.pool_w],
                    "pooling": pool, "sparsity": sparsity, "top_k": int(kv.shape[-1]), "flop_per_call": flops},
         "stage_ms": {k2: round(sum(v2) / len(v2), 4) for k2, v2 in times.items()},
         "roofline": {"bound": "mfma", "achieved": round(flops / (attn_avg * 1e-3) / 1e12, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(flops / (attn_avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic_for(w.name, ATTN_SRC), "kernel": "bsa_fwd_d128_kernel<MODE_LIST, true>"},
+                     "traffic": traffic_for(w.name, ATTN_SRC),
+                     "kernel": "bsa_fwd_d128_kernel<MODE_LIST, true>" if reorder else "bsa_fwd_d128_kernel<MODE_T2D, true>"},
     }
     return res
 
@@ -340,6 +355,8 @@ def main(argv=None) -> int:
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--sparsity", type=float, default=None, help="Draft workload: override the 90%% sparsity")
     ap.add_argument("--pool", choices=("mean", "max"), default="mean", help="Draft workload: pooling of Q and K")
+    ap.add_argument("--no-reorder", action="store_true",
+                    help="Draft workload: attend on the raster layout (draft_attn_fwd) instead of reordering")
     ap.add_argument("--dense-steps", type=int, default=3)
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="first run a plain row copy (token_permute, identity map) over this many MiB, 3 times, "

@@ -188,6 +188,25 @@ int block_sparse_attn_fwd(const void* q, const void* k, const void* v, float* o,
                           int block_q, int block_k, const int32_t* kv_idx, const int32_t* kv_cnt, int max_kv,
                           int mask_heads, const int32_t* block_valid, float scale, void* stream);
 
+/* Draft attention without the reorder  [DRAFT: blocks of the block-sparse
+ * kernel are the pool_h x pool_w tiles of the draft map; the reorder only
+ * makes each block contiguous]
+ *
+ * Same result as reordering Q, K, V (draft_mask_and_perm), running
+ * block_sparse_attn_fwd with block_q = block_k = pool_h*pool_w and
+ * block_valid, and scattering O back with token_permute, but on the raster
+ * layout: q, k, v [heads, T*H*grid_w, d] bf16 and o [heads, T*H*grid_w, d]
+ * fp32 in token order. Block b is tile (t, hb, wb) in raster order (as in
+ * draft_grid_info); its keys are the valid tokens of the tile, taken in
+ * (hi, wi) order; kv_idx [heads, nb, max_kv] and kv_cnt [heads, nb] are the
+ * per-head lists of draft_mask_and_perm (entries outside [0, nb) skipped).
+ * Every output row is written. Requires dt = LVSA_BF16, d = 128,
+ * pool_h*pool_w a multiple of 64 and pool_w dividing 64 (LVSA_EUNSUPPORTED
+ * otherwise); n*d < 2^30. */
+int draft_attn_fwd(const void* q, const void* k, const void* v, float* o, int dt, int heads, int T, int H,
+                   int grid_w, int d, int pool_h, int pool_w, const int32_t* kv_idx, const int32_t* kv_cnt,
+                   int max_kv, float scale, void* stream);
+
 /* Dense baseline: every query attends to all n keys. Same arithmetic and
  * layout as block_sparse_attn_fwd. */
 int dense_attn_fwd(const void* q, const void* k, const void* v, float* o, int dt, int heads, int n, int d,

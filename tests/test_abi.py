@@ -135,6 +135,24 @@ def test_mask_and_permute_validation(lib):
     assert dm(*bad, FAKE, need, None) == _lib.LVSA_EINVAL
     ds = lib.draft_scores
     assert ds(FAKE, FAKE, 1, 2, 3, 0, FAKE, None) == _lib.LVSA_EINVAL
+    da = lib.draft_attn_fwd
+    ok = [FAKE, FAKE, FAKE, FAKE, 1, 2, 3, 45, 80, 128, 8, 16, FAKE, FAKE, 99, 0.088, None]
+    for i, val, code in [(9, 64, _lib.LVSA_EUNSUPPORTED),   # d = 64
+                         (4, 0, _lib.LVSA_EUNSUPPORTED),    # fp32
+                         (10, 4, _lib.LVSA_EUNSUPPORTED),   # 4x16 = 64 slots: fine; pool 4x8 below
+                         (14, -1, _lib.LVSA_EINVAL),        # max_kv < 0
+                         (15, float("inf"), _lib.LVSA_EINVAL)]:
+        bad = list(ok)
+        bad[i] = val
+        if i == 10:
+            bad[11] = 8  # 4x8 = 32 slots: not a multiple of 64
+        assert da(*bad) == code, (i, val)
+    bad = list(ok)
+    bad[11] = 24  # 8x24 = 192 slots, but 24 does not divide 64
+    assert da(*bad) == _lib.LVSA_EUNSUPPORTED
+    bad = list(ok)
+    bad[13] = None  # kv_cnt
+    assert da(*bad) == _lib.LVSA_EINVAL
 
 
 @pytest.mark.skipif(not _no_gpu(), reason="checks the no-device error path")

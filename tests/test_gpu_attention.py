@@ -205,6 +205,49 @@ def test_draft_attention_small_all_rows(T, H, W, ph, pw, heads, d, sp):
         assert_attn_close(to_host(o), oracle.dense_attention(q, k, v), what="draft k=nb vs dense")
 
 
+@pytest.mark.parametrize("T,H,W,ph,pw,heads,sp", [
+    (3, 45, 80, 8, 16, 2, 0.9),   # HunyuanVideo frames (edge tiles of 5 rows)
+    (2, 20, 32, 8, 16, 2, 0.5),   # ragged tile rows, full-width tiles
+    (1, 8, 48, 4, 16, 3, 0.0),    # 64-token blocks, k = nb
+])
+def test_draft_raster_equals_reorder_path(T, H, W, ph, pw, heads, sp):
+    """With full-width tiles the reorder keeps each tile's tokens in raster
+    order, so attention on the raster layout sums the same keys in the same
+    tiles and order: the two paths agree bit for bit."""
+    torch = _torch()
+    q, k, v = _bf16_inputs(31, heads, T, H, W, 128)
+    note(f"draft raster vs reorder T={T} H={H} W={W} pool={ph}x{pw} heads={heads} sp={sp}")
+    out, op, o = _draft_pipeline(q, k, v, T, H, W, ph, pw, sp)
+    o2 = _lib.draft_attn_fwd(to_dev(q), to_dev(k), to_dev(v), T, H, W, ph, pw, out["kv_idx"], out["kv_cnt"])
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2)
+    g = oracle.draft_grid(T, H, W, ph, pw)
+    perm, inv, bv = oracle.draft_permutation(g)
+    rows = np.arange(0, g.N, 7)
+    ref = oracle.draft_attention_original_order(q, k, v, perm, inv, bv, g.block_size, to_host(out["kv_idx"]),
+                                                to_host(out["kv_cnt"]), rows=rows)
+    assert_attn_close(to_host(o2)[:, rows], ref, what="draft raster")
+
+
+@pytest.mark.parametrize("T,H,W,ph,pw,heads,sp", [
+    (2, 13, 21, 8, 8, 2, 0.5),    # 8-wide tiles (one tile row of 8 per 8 slots), ragged both ways
+    (2, 18, 40, 4, 16, 2, 0.7),   # 4x16 tiles, ragged columns (40 = 2*16 + 8)
+    (1, 9, 30, 8, 16, 2, 0.0),    # ragged rows and columns, k = nb
+])
+def test_draft_raster_vs_oracle_all_rows(T, H, W, ph, pw, heads, sp):
+    q, k, v = _bf16_inputs(32, heads, T, H, W, 128)
+    note(f"draft raster T={T} H={H} W={W} pool={ph}x{pw} heads={heads} sp={sp}")
+    out = _lib.draft_mask_and_perm(to_dev(q), to_dev(k), to_dev(v), T, H, W, ph, pw, sp, reorder=False)
+    o = _lib.draft_attn_fwd(to_dev(q), to_dev(k), to_dev(v), T, H, W, ph, pw, out["kv_idx"], out["kv_cnt"])
+    g = oracle.draft_grid(T, H, W, ph, pw)
+    perm, inv, bv = oracle.draft_permutation(g)
+    kv, cnt = to_host(out["kv_idx"]), to_host(out["kv_cnt"])
+    ref = oracle.draft_attention_original_order(q, k, v, perm, inv, bv, g.block_size, kv, cnt)
+    assert_attn_close(to_host(o), ref, what="draft raster")
+    if sp == 0.0:
+        assert_attn_close(to_host(o), oracle.dense_attention(q, k, v), what="draft raster k=nb vs dense")
+
+
 # ---------------------------------------------------------------------------
 # Full-size workloads, sampled rows.
 # ---------------------------------------------------------------------------
@@ -258,6 +301,21 @@ def test_full_hunyuan_draft():
     got = to_host(o)[heads][:, rows]
     assert_attn_close(got, ref, what="hunyuan draft")
     del out, op, o
+    torch.cuda.empty_cache()
+
+
+def test_full_hunyuan_draft_raster():
+    """Full HunyuanVideo size: the raster path equals the reorder path bit for bit."""
+    torch = _torch()
+    w, q, k, v = _full_inputs("hunyuan-draft")
+    note("hunyuan draft raster vs reorder, full size")
+    out, op, o = _draft_pipeline(q, k, v, w.T, w.H, w.W, w.pool_h, w.pool_w, w.sparsity)
+    del op
+    o2 = _lib.draft_attn_fwd(to_dev(q), to_dev(k), to_dev(v), w.T, w.H, w.W, w.pool_h, w.pool_w, out["kv_idx"],
+                             out["kv_cnt"])
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2)
+    del out, o, o2
     torch.cuda.empty_cache()
 
 

@@ -34,6 +34,7 @@ SIGNATURES = {
     "token_permute": (_c_int, [_p, _p] + [_c_int] * 5 + [_p, _p]),
     "block_sparse_attn_fwd": (_c_int, [_p] * 4 + [_c_int] * 6 + [_p, _p, _c_int, _c_int, _p, _c_flt, _p]),
     "dense_attn_fwd": (_c_int, [_p] * 4 + [_c_int] * 4 + [_c_flt, _p]),
+    "draft_attn_fwd": (_c_int, [_p] * 4 + [_c_int] * 8 + [_p, _p, _c_int, _c_flt, _p]),
 }
 
 _lib = None
@@ -236,4 +237,19 @@ def dense_attn_fwd(q, k, v, scale: float | None = None, out=None, stream=None):
     _contig_cuda(q, k, v, out)
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     _check(load().dense_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _dt(q), heads, n, d, scale, _stream(stream)))
+    return out
+
+
+def draft_attn_fwd(q, k, v, T: int, H: int, grid_w: int, pool_h: int, pool_w: int, kv_idx, kv_cnt,
+                   scale: float | None = None, out=None, stream=None):
+    """Draft attention on the raster layout (no reorder): q, k, v [heads, T*H*grid_w, 128]
+    bf16, per-head lists kv_idx [heads, nb, k], kv_cnt [heads, nb]; returns O fp32."""
+    torch = _torch()
+    heads, n, d = q.shape
+    if out is None:
+        out = torch.empty((heads, n, d), dtype=torch.float32, device=q.device)
+    _contig_cuda(q, k, v, out, kv_idx, kv_cnt)
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    _check(load().draft_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _dt(q), heads, T, H, grid_w, d, pool_h, pool_w,
+                                 _ptr(kv_idx), _ptr(kv_cnt), kv_idx.shape[-1], scale, _stream(stream)))
     return out

@@ -343,6 +343,62 @@ int block_sparse_attn_fwd(const void* q, const void* k, const void* v, float* o,
   return run_attn(a, dt, d, stream);
 }
 
+int draft_attn_fwd(const void* q, const void* k, const void* v, float* o, int dt, int heads, int T, int H,
+                   int grid_w, int d, int pool_h, int pool_w, const int32_t* kv_idx, const int32_t* kv_cnt,
+                   int max_kv, float scale, void* stream) {
+  clear_err();
+  lvsa::DraftGeom g;
+  int rc = geom(T, H, grid_w, pool_h, pool_w, &g);
+  if (rc) return rc;
+  rc = check_attn(q, k, v, o, dt, heads, g.n, d);
+  if (rc) return rc;
+  if (dt != LVSA_BF16 || d != 128) return fail(LVSA_EUNSUPPORTED, "draft_attn_fwd supports bf16 with d = 128");
+  if (g.bs % 64 != 0 || 64 % pool_w != 0)
+    return fail(LVSA_EUNSUPPORTED, "pool %dx%d: pool_h*pool_w must be a multiple of 64 and pool_w must divide 64",
+                pool_h, pool_w);
+  if (max_kv < 0) return fail(LVSA_EINVAL, "max_kv=%d must be >= 0", max_kv);
+  if (!std::isfinite(scale)) return fail(LVSA_EINVAL, "scale must be finite");
+  if (heads == 0) return LVSA_OK;
+  if (!kv_cnt || (max_kv > 0 && !kv_idx)) return fail(LVSA_EINVAL, "kv_cnt (and kv_idx when max_kv > 0) must be non-NULL");
+  if ((long long)max_kv * g.bs >= (1ll << 31)) return fail(LVSA_EINVAL, "key list spans more than 2^31 rows");
+  lvsa::AttnArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.heads = heads;
+  a.n = g.n;
+  a.block_q = g.bs;
+  a.block_k = g.bs;
+  a.nqb = g.nb;
+  a.nkb = g.nb;
+  a.kv_idx = kv_idx;
+  a.kv_cnt = kv_cnt;
+  a.max_kv = max_kv;
+  a.mask_heads = heads;
+  a.scale = scale;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.tile2d = 1;
+  a.gH = H;
+  a.gW = grid_w;
+  a.ph = pool_h;
+  a.pw = pool_w;
+  a.nbh = g.nbh;
+  a.nbw = g.nbw;
+  a.rpt = 64 / pool_w;
+  a.lpw = 0;
+  while ((1 << a.lpw) < pool_w) ++a.lpw;
+  a.inv_per = 1.0f / (float)(g.nbh * g.nbw);
+  a.inv_nbw = 1.0f / (float)g.nbw;
+  a.tiles_per_qb = (g.bs + lvsa::kBM_BF16 - 1) / lvsa::kBM_BF16;
+  const long long total = (long long)heads * g.nb * a.tiles_per_qb;
+  if (total >= (1ll << 31)) return fail(LVSA_EINVAL, "too many query tiles (%lld)", total);
+  a.total_tiles = (int)total;
+  rc = check_device();
+  if (rc) return rc;
+  return launched(lvsa::launch_draft_attn_bf16(a, reinterpret_cast<hipStream_t>(stream)), "draft attention launch");
+}
+
 int dense_attn_fwd(const void* q, const void* k, const void* v, float* o, int dt, int heads, int n, int d,
                    float scale, void* stream) {
   clear_err();

@@ -53,11 +53,14 @@ constexpr int kBM = kBM_BF16;
 constexpr unsigned kInvalid = 0x80000000u;  // byte offset past every buffer: loads return 0
 constexpr float kRescale = 8.0f;            // log2 headroom before the reference max moves
 
-enum { MODE_DENSE = 0, MODE_LIST = 1, MODE_SMALL = 2 };
+enum { MODE_DENSE = 0, MODE_LIST = 1, MODE_SMALL = 2, MODE_T2D = 3 };
 
 // Where the BN virtual key rows of one tile live. Uniform across the workgroup.
 // Row r < bnd is physical row base0 + r, row r >= bnd is base1 + r; row r is
 // a valid key iff r < rmax and (r < v0 or bnd <= r < v1).
+// MODE_T2D (a tile of a raster pool tile): bnd = pw; row r is token
+// base0 + (r / pw) * W + r % pw, valid iff r < rmax, r / pw < v0 and
+// r % pw < v1.
 struct TileD {
   int vt0;
   int base0, base1, bnd, v0, v1, rmax;
@@ -86,6 +89,32 @@ __device__ __forceinline__ int list_entry(const AttnArgs& a, const int32_t* list
   return (b < 0 || b >= a.nkb) ? -1 : b;
 }
 
+// Raster pool tile b = (t, hb, wb): its first token and valid rows/columns
+// (0, 0, 0 for b < 0).
+struct BlkGeom {
+  int tok, vh, vw;
+};
+// x / m for small x, m >= 1 (block indices: x < 4096): the float quotient is
+// within one of the exact one, which a single correction step fixes.
+__device__ __forceinline__ int div_small(int x, int m, float inv_m) {
+  int q = (int)((float)x * inv_m);
+  q -= (q * m > x);
+  q += ((q + 1) * m <= x);
+  return q;
+}
+
+__device__ __forceinline__ BlkGeom blk_geom(const AttnArgs& a, int b) {
+  BlkGeom g = {0, 0, 0};
+  if (b < 0) return g;
+  const int per = a.nbh * a.nbw;
+  const int t = div_small(b, per, a.inv_per), rb = b - t * per;
+  const int hb = div_small(rb, a.nbw, a.inv_nbw), wb = rb - hb * a.nbw;
+  g.tok = (t * a.gH + hb * a.ph) * a.gW + wb * a.pw;
+  g.vh = min(a.ph, a.gH - hb * a.ph);
+  g.vw = min(a.pw, a.gW - wb * a.pw);
+  return g;
+}
+
 // Walks the tiles of one key list in order. Advancing by one tile costs a
 // few scalar operations; only positioning at a start tile divides.
 struct TileStream {
@@ -93,6 +122,8 @@ struct TileStream {
   int slot, off;    // list slot of vt0 and the offset inside it
   int blk0, lim0;   // KV block of that slot and its valid rows
   int blk1, lim1;   // the same for the next slot
+  int r0;           // MODE_T2D: first tile row of the current tile
+  BlkGeom g0;       // MODE_T2D: geometry of blk0
 };
 
 template <int BN, int MODE>
@@ -101,13 +132,19 @@ __device__ __forceinline__ void stream_init(TileStream& ts, const AttnArgs& a, c
   ts.slot = ts.off = 0;
   ts.blk0 = ts.blk1 = -1;
   ts.lim0 = ts.lim1 = 0;
-  if (MODE == MODE_LIST) {
+  if (MODE == MODE_LIST || MODE == MODE_T2D) {
     ts.slot = ts.vt0 / a.block_k;
     ts.off = ts.vt0 - ts.slot * a.block_k;
     ts.blk0 = list_entry(a, list, cnt, ts.slot);
-    ts.lim0 = block_lim(a, ts.blk0);
     ts.blk1 = list_entry(a, list, cnt, ts.slot + 1);
+  }
+  if (MODE == MODE_LIST) {
+    ts.lim0 = block_lim(a, ts.blk0);
     ts.lim1 = block_lim(a, ts.blk1);
+  }
+  if (MODE == MODE_T2D) {
+    ts.r0 = ts.off >> a.lpw;
+    ts.g0 = blk_geom(a, ts.blk0);
   }
 }
 
@@ -123,6 +160,18 @@ __device__ __forceinline__ void stream_next(TileStream& ts, const AttnArgs& a, c
       ts.lim0 = ts.lim1;
       ts.blk1 = list_entry(a, list, cnt, ts.slot + 1);
       ts.lim1 = block_lim(a, ts.blk1);
+    }
+  }
+  if (MODE == MODE_T2D) {
+    ts.off += BN;
+    ts.r0 += a.rpt;
+    if (ts.off >= a.block_k) {  // block_k is a multiple of BN: the tile starts the next slot
+      ts.off = 0;
+      ts.r0 = 0;
+      ts.slot += 1;
+      ts.blk0 = ts.blk1;
+      ts.g0 = blk_geom(a, ts.blk0);
+      ts.blk1 = list_entry(a, list, cnt, ts.slot + 1);
     }
   }
 }
@@ -145,6 +194,13 @@ __device__ __forceinline__ TileD stream_tile(const TileStream& ts, const AttnArg
     t.v0 = min(t.bnd, ts.lim0 - ts.off);
     t.v1 = t.bnd + ts.lim1;
     t.full = t.rmax >= BN && t.v0 >= min(t.bnd, BN) && (t.bnd >= BN || t.v1 >= BN);
+  } else if (MODE == MODE_T2D) {
+    t.bnd = a.pw;
+    t.base0 = ts.g0.tok + ts.r0 * a.gW;
+    t.base1 = 0;
+    t.v0 = max(0, min(a.rpt, ts.g0.vh - ts.r0));
+    t.v1 = ts.g0.vw;
+    t.full = t.rmax >= BN && t.v0 == a.rpt && t.v1 == a.pw;
   } else {
     t.base0 = t.base1 = t.bnd = t.v0 = t.v1 = 0;
     t.full = 0;
@@ -162,6 +218,11 @@ __device__ __forceinline__ int tile_row(const AttnArgs& a, const TileD& t, const
     const int off = vj - slot * a.block_k;
     const int blk = list_entry(a, list, cnt, slot);
     return off < block_lim(a, blk) ? blk * a.block_k + off : -1;
+  }
+  if (MODE == MODE_T2D) {
+    const int hi = r >> a.lpw, wi = r & (t.bnd - 1);
+    const bool ok2 = (r < t.rmax) & (hi < t.v0) & (wi < t.v1);
+    return ok2 ? t.base0 + hi * a.gW + wi : -1;
   }
   const bool ok = (r < t.rmax) & ((r < t.v0) | ((r >= t.bnd) & (r < t.v1)));
   const int p = (r < t.bnd ? t.base0 : t.base1) + r;
@@ -563,10 +624,23 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_d128_kernel(AttnArgs a) {
   }
   const int qend = min(blk_lo + qlim, blk_end);
   const int row_lo = blk_lo + qt * kBM;
-  const int qrow = row_lo + wave * 32 + l32;
-  const bool active = !SKIP || row_lo + wave * 32 < qend;
-  const bool q_in_blk = qrow < blk_end;
-  const bool q_valid = qrow < qend;
+  int qrow = row_lo + wave * 32 + l32;
+  bool active = !SKIP || row_lo + wave * 32 < qend;
+  bool q_in_blk = qrow < blk_end;
+  bool q_valid = qrow < qend;
+  bool no_queries = row_lo >= qend;
+  if (MODE == MODE_T2D) {
+    // Query block qb is a raster pool tile; slot s = (s / pw, s % pw).
+    const BlkGeom gq = blk_geom(a, qb);
+    const int s0 = qt * kBM;
+    const int slot = s0 + wave * 32 + l32;
+    const int hi = slot >> a.lpw, wi = slot & (a.pw - 1);
+    q_valid = slot < a.block_q && hi < gq.vh && wi < gq.vw;
+    q_in_blk = q_valid;
+    qrow = q_valid ? gq.tok + hi * a.gW + wi : 0;
+    active = !SKIP || ((s0 + wave * 32) >> a.lpw) < gq.vh;
+    no_queries = (s0 >> a.lpw) >= gq.vh;
+  }
 
   const size_t head_off = (size_t)h * (size_t)a.n * D;
   const int head_bytes = a.n * D * 2;
@@ -588,7 +662,7 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_d128_kernel(AttnArgs a) {
     list = a.kv_idx + (size_t)base * a.max_kv;
     L = cnt * a.block_k;
   }
-  if (row_lo >= qend) L = 0;
+  if (no_queries) L = 0;
   const int ntiles = (L + BN - 1) / BN;
 
   bf16x8 qreg[KSTEPS];
@@ -618,7 +692,10 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_d128_kernel(AttnArgs a) {
     vra[db] = (unsigned)((4 * (tg >> 1) + (ti >> 2)) * 256 +
                          16 * ((4 * db + 2 * (tg & 1) + ((ti & 3) >> 1)) ^ gv_swz(ti >> 2)) + 8 * (ti & 1));
 
-  auto simple = [&](const TileD& t) { return t.full && t.bnd >= BN; };
+  // A tile whose 64 rows are valid and are 4 runs of 16 consecutive rows of
+  // K/V (one run per DMA instruction) loads with one scalar offset per run.
+  auto simple = [&](const TileD& t) { return MODE == MODE_T2D ? (t.full && a.pw == 16) : (t.full && t.bnd >= BN); };
+  const unsigned run_bytes = MODE == MODE_T2D ? (unsigned)a.gW * D * 2 : 4096u;
   auto dma = [&](__amdgpu_buffer_rsrc_t r, int st, int kind, int j, unsigned voff, unsigned soff) {
     unsigned char* dst = (kind == 0 ? kbuf(st) : vbuf(st)) + 4096 * j + 1024 * wave;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, voff, soff, 0, 0);
@@ -627,7 +704,7 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_d128_kernel(AttnArgs a) {
     if (simple(t)) {
       const unsigned so = (unsigned)(t.base0 * D * 2);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) dma(Kr, st, 0, j, kdma, so + 4096u * j);
+      for (int j = 0; j < 4; ++j) dma(Kr, st, 0, j, kdma, so + run_bytes * j);
     } else {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -641,7 +718,7 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_d128_kernel(AttnArgs a) {
     if (simple(t)) {
       const unsigned so = (unsigned)(t.base0 * D * 2);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) dma(Vr, st, 1, j, vdma, so + 4096u * j);
+      for (int j = 0; j < 4; ++j) dma(Vr, st, 1, j, vdma, so + run_bytes * j);
     } else {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -783,6 +860,18 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_d128_kernel(AttnArgs a) {
 
   const float l_tot = half_sum(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (MODE == MODE_T2D) {
+    // Recompute the output row from an opaque copy of the lane id rather
+    // than keep it live through the key walk.
+    int lid = l32;
+    asm volatile("" : "+v"(lid));
+    const BlkGeom gq = blk_geom(a, qb);
+    const int slot = qt * kBM + wave * 32 + lid;
+    const int hi = slot >> a.lpw, wi = slot & (a.pw - 1);
+    q_valid = slot < a.block_q && hi < gq.vh && wi < gq.vw;
+    q_in_blk = q_valid;
+    qrow = q_valid ? gq.tok + hi * a.gW + wi : 0;
+  }
   if (q_in_blk) {
     float* orow = Oh + (size_t)qrow * D;
 #pragma unroll
@@ -826,6 +915,12 @@ hipError_t launch_d128(const AttnArgs& a, hipStream_t s) {
     hipLaunchKernelGGL((bsa_fwd_d128_kernel<MODE_LIST, false>), grid, block, 0, s, a);
   else
     hipLaunchKernelGGL((bsa_fwd_d128_kernel<MODE_SMALL, false>), grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_draft_attn_bf16(const AttnArgs& a, hipStream_t s) {
+  if (a.total_tiles == 0) return hipSuccess;
+  hipLaunchKernelGGL((bsa_fwd_d128_kernel<MODE_T2D, false>), dim3(a.total_tiles), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

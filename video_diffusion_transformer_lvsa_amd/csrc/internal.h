@@ -31,6 +31,14 @@ struct AttnArgs {
   float scale_log2;            // softmax scale * log2(e)
   float scale;                 // softmax scale
   int dense;                   // 1: every query sees all n keys
+  // Blocks as pool_h x pool_w tiles of a [T, H, W] raster grid (draft_attn_fwd;
+  // tile2d = 0 otherwise): block b = (t, hb, wb) in raster order, block_q =
+  // block_k = ph*pw slots, slot s = (s / pw, s % pw) inside the tile.
+  int tile2d;
+  int gH, gW, ph, pw, nbh, nbw;
+  int rpt;  // tile rows per 64-slot key tile (64 / pw)
+  int lpw;  // log2(pw): pw divides 64
+  float inv_per, inv_nbw;  // 1 / (nbh * nbw), 1 / nbw: block index -> (t, hb, wb)
 };
 
 // Query rows per workgroup of the bf16 MFMA kernel and of the fp32 kernel.
@@ -38,6 +46,8 @@ constexpr int kBM_BF16 = 128;
 constexpr int kBM_F32 = 64;
 
 hipError_t launch_attn_bf16(const AttnArgs& a, int d, hipStream_t s);
+// Draft attention on the raster layout (d = 128, bf16): a.tile2d = 1.
+hipError_t launch_draft_attn_bf16(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_f32(const AttnArgs& a, int d, hipStream_t s);
 
 hipError_t launch_lvsa_mask(int T, int C, int window, int T_per, int step, int32_t* kv_idx, int32_t* kv_cnt,
