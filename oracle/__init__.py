@@ -38,6 +38,7 @@ from .draft import (
     draft_topk,
     draft_mask,
 )
+from .fp8 import E4M3_MAX, e4m3_decode_table, e4m3_encode, quantize_per_head, dequantize
 from .attention import (
     attention_keyset,
     dense_attention,
@@ -47,6 +48,11 @@ from .attention import (
 )
 
 __all__ = [
+    "E4M3_MAX",
+    "e4m3_decode_table",
+    "e4m3_encode",
+    "quantize_per_head",
+    "dequantize",
     "anchors",
     "nearest_order",
     "attend_set",
