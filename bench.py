@@ -29,9 +29,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
+PEAK_FP8_TFLOPS = 5033.2   # dense fp8 MFMA: twice the bf16 rate
 PEAK_HBM_GBS = 8000.0
 METRIC = "block-sparse attn ms/call + effective TFLOP/s (% bf16 MFMA peak), 1 MI355X"
 ATTN_SRC = os.path.join(ROOT, "video_diffusion_transformer_lvsa_amd", "csrc", "attn_bf16.hip")
+ATTN_FP8_SRC = os.path.join(ROOT, "video_diffusion_transformer_lvsa_amd", "csrc", "attn_fp8.hip")
 DRAFT_SRC = os.path.join(ROOT, "video_diffusion_transformer_lvsa_amd", "csrc", "draft.hip")
 
 WORKLOAD_NAMES = {
@@ -151,9 +153,36 @@ def run_lvsa(args, w):
     kv_cnt = torch.empty((w.T,), dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream()
 
+    fp8 = bool(args.fp8)
+    if fp8:
+        # E4M3 codes (V transposed) and per-head scales, refreshed every step
+        q8 = torch.empty((w.heads, w.N, w.d), dtype=torch.uint8, device=dev)
+        k8 = torch.empty_like(q8)
+        vt8 = torch.empty((w.heads, w.d, _lib.fp8_pitch(w.N)), dtype=torch.uint8, device=dev)
+        sc = torch.empty((3, w.heads), dtype=torch.float32, device=dev)
+
+    def quantize():
+        _lib.quantize_fp8_e4m3(dq, out=q8, scales=sc[0])
+        _lib.quantize_fp8_e4m3(dk, out=k8, scales=sc[1])
+        _lib.quantize_fp8_e4m3(dv, transpose=True, out=vt8, scales=sc[2])
+
+    def attn():
+        if fp8:
+            _lib.block_sparse_attn_fwd_fp8(q8, k8, vt8, sc[0], sc[1], sc[2], w.P, w.P, kv_idx, kv_cnt, out=o)
+        else:
+            _lib.block_sparse_attn_fwd(dq, dk, dv, w.P, w.P, kv_idx, kv_cnt, out=o)
+
+    def dense():
+        if fp8:
+            _lib.dense_attn_fwd_fp8(q8, k8, vt8, sc[0], sc[1], sc[2], out=o)
+        else:
+            _lib.dense_attn_fwd(dq, dk, dv, out=o)
+
     def step(i):
+        if fp8:
+            quantize()
         _lib.lvsa_mask(w.T, w.C, w.window, w.T_per, i % w.T_per, cap=cap, kv_idx=kv_idx, kv_cnt=kv_cnt)
-        _lib.block_sparse_attn_fwd(dq, dk, dv, w.P, w.P, kv_idx, kv_cnt, out=o)
+        attn()
 
     log("warmup")
     for i in range(args.warmup):
@@ -172,11 +201,16 @@ def run_lvsa(args, w):
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record(stream)
+    qev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     for i in range(args.steps):
         s = (args.warmup + i) % w.T_per
+        if fp8:
+            qev[i][0].record(stream)
+            quantize()
+            qev[i][1].record(stream)
         _lib.lvsa_mask(w.T, w.C, w.window, w.T_per, s, cap=cap, kv_idx=kv_idx, kv_cnt=kv_cnt)
         ev[i][0].record(stream)
-        _lib.block_sparse_attn_fwd(dq, dk, dv, w.P, w.P, kv_idx, kv_cnt, out=o)
+        attn()
         ev[i][1].record(stream)
         total_pairs += pairs[s]
     t1.record(stream)
@@ -189,7 +223,9 @@ def run_lvsa(args, w):
     attn_avg = sum(attn_ms) / len(attn_ms)
     flop_per_launch = flops_total / args.steps
     achieved = flop_per_launch / (attn_avg * 1e-3) / 1e12
-    mask_ms = ms_per_step - attn_avg
+    quant_ms = sum(a.elapsed_time(b) for a, b in qev) / args.steps if fp8 else 0.0
+    mask_ms = ms_per_step - attn_avg - quant_ms
+    peak = PEAK_FP8_TFLOPS if fp8 else PEAK_BF16_TFLOPS
 
     res = {
         "metric": METRIC,
@@ -202,10 +238,10 @@ def run_lvsa(args, w):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8-e4m3" if fp8 else "bf16",
         "data": "synthetic",
         "config": {
-            "workload": WORKLOAD_NAMES[w.name],
+            "workload": WORKLOAD_NAMES[w.name] + ("-fp8" if fp8 else ""),
             "T": w.T, "H": w.H, "W": w.W, "tokens": w.N, "heads": w.heads, "d": w.d,
             "C": w.C, "window": w.window, "T_per": w.T_per, "steps_s": "s = step mod T_per",
             "flop_per_call": flop_per_launch,
@@ -215,26 +251,29 @@ def run_lvsa(args, w):
         "mask_build_ms": round(max(mask_ms, 0.0), 4),
         "pct_bf16_peak": round(100.0 * achieved / PEAK_BF16_TFLOPS, 2),
     }
+    if fp8:
+        res["quantize_ms"] = round(quant_ms, 4)
+        res["pct_fp8_peak"] = round(100.0 * achieved / PEAK_FP8_TFLOPS, 2)
     res["roofline"] = {
         "bound": "mfma",
         "achieved": round(achieved, 2),
-        "peak": PEAK_BF16_TFLOPS,
+        "peak": peak,
         "unit": "TFLOP/s",
-        "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-        "traffic": traffic_for(w.name, ATTN_SRC),
-        "kernel": "bsa_fwd_d128_kernel<MODE_LIST, false>",
+        "frac": round(achieved / peak, 4),
+        "traffic": traffic_for(w.name + ("-fp8" if fp8 else ""), ATTN_FP8_SRC if fp8 else ATTN_SRC),
+        "kernel": "bsa_fwd_fp8_kernel<MODE_LIST>" if fp8 else "bsa_fwd_d128_kernel<MODE_LIST, false>",
     }
 
     if not args.no_dense:
         log("timing dense attention at the same shape")
-        _lib.dense_attn_fwd(dq, dk, dv, out=o)
+        dense()
         torch.cuda.synchronize()
         d0 = torch.cuda.Event(enable_timing=True)
         d1 = torch.cuda.Event(enable_timing=True)
         nd = args.dense_steps
         d0.record(stream)
         for _ in range(nd):
-            _lib.dense_attn_fwd(dq, dk, dv, out=o)
+            dense()
         d1.record(stream)
         torch.cuda.synchronize()
         dense_ms = d0.elapsed_time(d1) / nd
@@ -358,6 +397,8 @@ def main(argv=None) -> int:
     ap.add_argument("--no-reorder", action="store_true",
                     help="Draft workload: attend on the raster layout (draft_attn_fwd) instead of reordering")
     ap.add_argument("--dense-steps", type=int, default=3)
+    ap.add_argument("--fp8", action="store_true",
+                    help="LVSA workloads: quantize Q, K, V to E4M3 each step and run the FP8 attention")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="first run a plain row copy (token_permute, identity map) over this many MiB, 3 times, "
                          "so HBM counters can be scaled by a kernel of known traffic")

@@ -212,6 +212,54 @@ int draft_attn_fwd(const void* q, const void* k, const void* v, float* o, int dt
 int dense_attn_fwd(const void* q, const void* k, const void* v, float* o, int dt, int heads, int n, int d,
                    float scale, void* stream);
 
+/* ------------------------------------------------------------------------
+ * FP8 (OCP E4M3) variant  [DRAFT: the article names quantization as the
+ * step after its sparse mask; it fixes no format, so the choices below are
+ * this library's]
+ *
+ * Format: E4M3 "fn" bytes (1 sign, 4 exponent bits with bias 7, 3 mantissa
+ * bits, subnormals, largest finite 448, no infinity; 0x7F/0xFF are NaN and
+ * never produced). One dequantization factor per (tensor, head).
+ * ------------------------------------------------------------------------ */
+
+/* Per-head quantization of src [heads, n, d] (dt bf16 or fp32, finite
+ * values): scale[h] = fl32(max|src[h]| / 448) (1 when the head is all
+ * zeros), code = the E4M3 value nearest fl32(x / scale[h]) after clamping
+ * the quotient to [-448, 448], ties to the even mantissa; the value a code
+ * stands for is decode(code) * scale[h].
+ * transpose = 0: dst [heads, n, d], ld must be 0.
+ * transpose = 1: dst [heads, d, ld], dst[h, c, i] = code of src[h, i, c];
+ *   ld (row pitch in bytes) a multiple of 16 and >= n; bytes n .. ld-1 of a
+ *   row are left as they are. This is the layout the attention takes V in.
+ * scales: device float[heads], written. d is 64 or 128; n*d < 2^30 and
+ * d*ld < 2^31. src, dst 16-byte aligned; scales 4-byte aligned. */
+int quantize_fp8_e4m3(const void* src, int dt, int heads, int n, int d, int transpose, int ld, uint8_t* dst,
+                      float* scales, void* stream);
+
+/* Block-sparse attention on E4M3 operands: q8, k8 [heads, n, 128] codes,
+ * vt8 [heads, 128, ldv] codes of Vᵀ (quantize_fp8_e4m3 with transpose = 1),
+ * q_scale, k_scale, v_scale device float[heads]. Same key lists, masking
+ * and output layout as block_sparse_attn_fwd (block_valid is not taken),
+ * on the values q = q_scale[h] * decode(q8) (likewise k, v):
+ *   s_ij = scale * <q_i, k_j> (exact products, fp32 sums, on the FP8
+ *   matrix cores), probabilities exp(s_ij - m) in fp32 with m the running
+ *   maximum (updated only when it grows by more than 2^8 in base 2), the
+ *   probabilities rounded to E4M3 (nearest even) for the PV product, the row
+ *   sum over the unrounded fp32 values, O fp32 [heads, n, 128].
+ * Requires d = 128, n a multiple of 4, block_k >= 64 and a multiple of 4
+ * (LVSA_EUNSUPPORTED otherwise); ldv a multiple of 16, >= n (LVSA_EINVAL);
+ * n*128 < 2^30. */
+int block_sparse_attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* vt8, int ldv,
+                              const float* q_scale, const float* k_scale, const float* v_scale, float* o, int heads,
+                              int n, int d, int block_q, int block_k, const int32_t* kv_idx, const int32_t* kv_cnt,
+                              int max_kv, int mask_heads, float scale, void* stream);
+
+/* Dense FP8 attention: every query attends to all n keys; arithmetic and
+ * layouts as block_sparse_attn_fwd_fp8 (d = 128, n a multiple of 4). */
+int dense_attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* vt8, int ldv, const float* q_scale,
+                       const float* k_scale, const float* v_scale, float* o, int heads, int n, int d, float scale,
+                       void* stream);
+
 #ifdef __cplusplus
 }
 #endif

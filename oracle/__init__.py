@@ -38,7 +38,7 @@ from .draft import (
     draft_topk,
     draft_mask,
 )
-from .fp8 import E4M3_MAX, e4m3_decode_table, e4m3_encode, quantize_per_head, dequantize
+from .fp8 import E4M3_MAX, e4m3_decode_table, e4m3_encode, quantize_per_head, dequantize, attention_p_e4m3, p_rounding_bound
 from .attention import (
     attention_keyset,
     dense_attention,
@@ -53,6 +53,8 @@ __all__ = [
     "e4m3_encode",
     "quantize_per_head",
     "dequantize",
+    "attention_p_e4m3",
+    "p_rounding_bound",
     "anchors",
     "nearest_order",
     "attend_set",

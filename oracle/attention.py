@@ -51,8 +51,11 @@ def _chunks(rows: np.ndarray, size: int):
         yield rows[i : i + size]
 
 
-def dense_attention(q, k, v, scale: float | None = None, rows=None, heads=None, chunk: int = 512) -> np.ndarray:
-    """Dense attention; q, k, v [heads, N, d] (bf16 bits or float). Returns fp64 [len(heads), len(rows), d]."""
+def dense_attention(q, k, v, scale: float | None = None, rows=None, heads=None, chunk: int = 512,
+                    fn=None) -> np.ndarray:
+    """Dense attention; q, k, v [heads, N, d] (bf16 bits or float). Returns fp64 [len(heads), len(rows), d].
+    fn(q_rows, k_sel, v_sel, scale) evaluates a row set over its keys (default: attention_keyset)."""
+    fn = attention_keyset if fn is None else fn
     H, n, d = q.shape
     scale = 1.0 / np.sqrt(d) if scale is None else scale
     rows = np.arange(n) if rows is None else np.asarray(rows)
@@ -61,7 +64,7 @@ def dense_attention(q, k, v, scale: float | None = None, rows=None, heads=None, 
     for hi, h in enumerate(heads):
         kh, vh = to_f64(k[h]), to_f64(v[h])
         for ci, r in enumerate(_chunks(rows, chunk)):
-            out[hi, ci * chunk : ci * chunk + len(r)] = attention_keyset(to_f64(q[h, r]), kh, vh, scale)
+            out[hi, ci * chunk : ci * chunk + len(r)] = fn(to_f64(q[h, r]), kh, vh, scale)
     return out
 
 
@@ -78,7 +81,8 @@ def _block_keys(blocks, block_k: int, n: int, block_valid) -> np.ndarray:
 
 
 def block_sparse_attention(q, k, v, block_q: int, block_k: int, kv_idx, kv_cnt, mask_heads: int = 1,
-                           block_valid=None, scale: float | None = None, rows=None, heads=None) -> np.ndarray:
+                           block_valid=None, scale: float | None = None, rows=None, heads=None,
+                           fn=None) -> np.ndarray:
     """Block-sparse attention in the layout given.
 
     Query row i of head h belongs to query block i // block_q; its keys are
@@ -86,7 +90,9 @@ def block_sparse_attention(q, k, v, block_q: int, block_k: int, kv_idx, kv_cnt, 
     hm = h if mask_heads > 1 else 0 (each block contributes the rows
     [b*block_k, b*block_k + valid(b)) inside [0, n), valid(b) = block_valid[b]
     or block_k). A query row at a slot >= block_valid of its block is a pad
-    and gets output 0. Returns fp64 [len(heads), len(rows), d]."""
+    and gets output 0. Returns fp64 [len(heads), len(rows), d]. fn evaluates a
+    row set over its keys (default: attention_keyset)."""
+    fn = attention_keyset if fn is None else fn
     H, n, d = q.shape
     scale = 1.0 / np.sqrt(d) if scale is None else scale
     kv_idx = np.asarray(kv_idx)
@@ -109,7 +115,7 @@ def block_sparse_attention(q, k, v, block_q: int, block_k: int, kv_idx, kv_cnt, 
             if len(r) == 0:
                 continue
             keys = _block_keys(kv_idx[hm, qb, : int(kv_cnt[hm, qb])], block_k, n, block_valid)
-            out[hi, sel] = attention_keyset(to_f64(q[h, r]), to_f64(k[h, keys]), to_f64(v[h, keys]), scale)
+            out[hi, sel] = fn(to_f64(q[h, r]), to_f64(k[h, keys]), to_f64(v[h, keys]), scale)
     return out
 
 

@@ -89,3 +89,50 @@ def dequantize(codes: np.ndarray, scales: np.ndarray, transposed: bool = False) 
     if transposed:
         c = c.transpose(0, 2, 1)
     return _TABLE[c] * np.asarray(scales, dtype=np.float64)[:, None, None]
+
+
+def attention_p_e4m3(q_rows: np.ndarray, k_sel: np.ndarray, v_sel: np.ndarray, scale: float) -> np.ndarray:
+    """Softmax attention with the probabilities rounded to E4M3 for the PV
+    product: p_j = exp(s_j - max_k s_k), O = sum_j e4m3(p_j) v_j / sum_j p_j
+    (the row sum over the unrounded p). The plain statement of the FP8
+    attention's arithmetic, with the row maximum as the reference; a kernel
+    that takes another reference score r (x_j - r <= 8 in base 2) rounds other
+    values and differs from this by at most twice p_rounding_bound. Same
+    arguments as attention.attention_keyset; returns fp64 [m, d]."""
+    q_rows = np.asarray(q_rows, dtype=np.float64)
+    k_sel = np.asarray(k_sel, dtype=np.float64)
+    v_sel = np.asarray(v_sel, dtype=np.float64)
+    if k_sel.shape[0] == 0:
+        return np.zeros((q_rows.shape[0], v_sel.shape[1]), dtype=np.float64)
+    s = (q_rows @ k_sel.T) * scale
+    p = np.exp(s - s.max(axis=1, keepdims=True))
+    pr = _TABLE[e4m3_encode(p.astype(np.float32))]
+    return (pr @ v_sel) / p.sum(axis=1, keepdims=True)
+
+
+def p_rounding_bound(q_rows: np.ndarray, k_sel: np.ndarray, v_sel: np.ndarray, scale: float) -> np.ndarray:
+    """Per-element bound on |O~ - O| for softmax attention whose probabilities
+    are rounded to E4M3 (nearest) before the PV product while the row sum
+    keeps the unrounded values; everything else exact. Same arguments as
+    attention.attention_keyset (values, not codes); returns fp64 [m, d].
+
+    Derivation (the reading this library takes for its FP8 attention): the
+    probabilities are p_j = 2^(x_j - r) with x_j the base-2 scores and r one
+    of the row's scores, r <= max_j x_j and x_j - r <= 8, so p_j <= 2^8 < 448
+    and max_j p_j >= 1. Rounding to E4M3 moves p by at most 2^-4 p in the
+    normal range (p >= 2^-6: 3 mantissa bits), by at most 2^-10 in the
+    subnormal range (step 2^-9), and by at most p itself (p < 2^-10 rounds
+    to 0): |p~ - p| <= 2^-4 p + min(p, 2^-10). With w the softmax weights,
+    p_j = w_j sum_k p_k, and sum_k p_k >= 1 / w_max (since max_j p_j >= 1):
+        |O~_c - O_c| <= sum_j |p~_j - p_j| |v_jc| / sum_k p_k
+                     <= 2^-4 sum_j w_j |v_jc| + sum_j min(w_j, 2^-10 w_max) |v_jc|."""
+    q_rows = np.asarray(q_rows, dtype=np.float64)
+    k_sel = np.asarray(k_sel, dtype=np.float64)
+    v_abs = np.abs(np.asarray(v_sel, dtype=np.float64))
+    if k_sel.shape[0] == 0:
+        return np.zeros((q_rows.shape[0], v_abs.shape[1]), dtype=np.float64)
+    s = (q_rows @ k_sel.T) * scale
+    e = np.exp(s - s.max(axis=1, keepdims=True))
+    w = e / e.sum(axis=1, keepdims=True)
+    small = np.minimum(w, 2.0 ** -10 * w.max(axis=1, keepdims=True))
+    return 2.0 ** -4 * (w @ v_abs) + small @ v_abs

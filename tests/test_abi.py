@@ -155,8 +155,63 @@ def test_mask_and_permute_validation(lib):
     assert da(*bad) == _lib.LVSA_EINVAL
 
 
+def test_fp8_validation(lib):
+    qz = lib.quantize_fp8_e4m3
+    ok = [FAKE, 1, 2, 256, 128, 1, 256, FAKE, FAKE, None]
+    for i, val, code in [(1, 7, _lib.LVSA_EINVAL),          # dtype
+                         (4, 96, _lib.LVSA_EUNSUPPORTED),   # d
+                         (5, 2, _lib.LVSA_EINVAL),          # transpose flag
+                         (6, 200, _lib.LVSA_EINVAL),        # ld < n
+                         (6, 264, _lib.LVSA_EINVAL),        # ld not a multiple of 16
+                         (0, None, _lib.LVSA_EINVAL),       # src
+                         (7, MIS, _lib.LVSA_EINVAL),        # dst misaligned
+                         (8, None, _lib.LVSA_EINVAL),       # scales
+                         (3, 1 << 23, _lib.LVSA_EINVAL)]:   # n*d >= 2^30
+        bad = list(ok)
+        bad[i] = val
+        assert qz(*bad) == code, (i, val)
+    row = list(ok)
+    row[5], row[6] = 0, 16  # ld must be 0 without transpose
+    assert qz(*row) == _lib.LVSA_EINVAL
+    empty = list(ok)
+    empty[2] = 0
+    assert qz(*empty) == 0
+
+    bs = lib.block_sparse_attn_fwd_fp8
+    ok = [FAKE, FAKE, FAKE, 1568, FAKE, FAKE, FAKE, FAKE, 2, 1560, 128, 1560, 1560, FAKE, FAKE, 3, 1, 0.088, None]
+    for i, val, code in [(10, 64, _lib.LVSA_EUNSUPPORTED),   # d
+                         (9, 1558, _lib.LVSA_EUNSUPPORTED),  # n not a multiple of 4
+                         (3, 1552, _lib.LVSA_EINVAL),        # ldv < n
+                         (3, 1570, _lib.LVSA_EINVAL),        # ldv not a multiple of 16
+                         (12, 32, _lib.LVSA_EUNSUPPORTED),   # block_k < 64
+                         (12, 66, _lib.LVSA_EUNSUPPORTED),   # block_k not a multiple of 4
+                         (11, 0, _lib.LVSA_EINVAL),          # block_q
+                         (16, 3, _lib.LVSA_EINVAL),          # mask_heads
+                         (15, -1, _lib.LVSA_EINVAL),         # max_kv
+                         (17, float("nan"), _lib.LVSA_EINVAL),
+                         (4, None, _lib.LVSA_EINVAL),        # q_scale
+                         (0, MIS, _lib.LVSA_EINVAL),         # q8 misaligned
+                         (14, None, _lib.LVSA_EINVAL)]:      # kv_cnt
+        bad = list(ok)
+        bad[i] = val
+        assert bs(*bad) == code, (i, val)
+    empty = list(ok)
+    empty[8] = 0
+    assert bs(*empty) == 0
+    dn = lib.dense_attn_fwd_fp8
+    ok = [FAKE, FAKE, FAKE, 1008, FAKE, FAKE, FAKE, FAKE, 2, 1000, 128, 0.088, None]
+    assert dn(*(ok[:10] + [64] + ok[11:])) == _lib.LVSA_EUNSUPPORTED
+    assert dn(*(ok[:9] + [1002] + ok[10:])) == _lib.LVSA_EUNSUPPORTED
+    assert dn(*(ok[:3] + [1000] + ok[4:])) == _lib.LVSA_EINVAL
+    assert dn(*(ok[:6] + [None] + ok[7:])) == _lib.LVSA_EINVAL
+    assert dn(*(ok[:8] + [0] + ok[9:])) == 0
+
+
 @pytest.mark.skipif(not _no_gpu(), reason="checks the no-device error path")
 def test_no_device_is_reported(lib):
     assert lib.lvsa_mask(4, 3, 2, 2, 0, FAKE, FAKE, 3, None) == _lib.LVSA_EDEVICE
     assert "GPU" in _lib.last_error()
     assert lib.dense_attn_fwd(FAKE, FAKE, FAKE, FAKE, 1, 2, 256, 128, 0.1, None) == _lib.LVSA_EDEVICE
+    assert lib.quantize_fp8_e4m3(FAKE, 1, 2, 256, 128, 1, 256, FAKE, FAKE, None) == _lib.LVSA_EDEVICE
+    assert lib.dense_attn_fwd_fp8(FAKE, FAKE, FAKE, 256, FAKE, FAKE, FAKE, FAKE, 2, 256, 128, 0.1,
+                                  None) == _lib.LVSA_EDEVICE

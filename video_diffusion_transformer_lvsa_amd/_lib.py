@@ -35,6 +35,10 @@ SIGNATURES = {
     "block_sparse_attn_fwd": (_c_int, [_p] * 4 + [_c_int] * 6 + [_p, _p, _c_int, _c_int, _p, _c_flt, _p]),
     "dense_attn_fwd": (_c_int, [_p] * 4 + [_c_int] * 4 + [_c_flt, _p]),
     "draft_attn_fwd": (_c_int, [_p] * 4 + [_c_int] * 8 + [_p, _p, _c_int, _c_flt, _p]),
+    "quantize_fp8_e4m3": (_c_int, [_p] + [_c_int] * 6 + [_p, _p, _p]),
+    "block_sparse_attn_fwd_fp8": (_c_int, [_p] * 3 + [_c_int] + [_p] * 4 + [_c_int] * 5
+                                  + [_p, _p, _c_int, _c_int, _c_flt, _p]),
+    "dense_attn_fwd_fp8": (_c_int, [_p] * 3 + [_c_int] + [_p] * 4 + [_c_int] * 3 + [_c_flt, _p]),
 }
 
 _lib = None
@@ -252,4 +256,71 @@ def draft_attn_fwd(q, k, v, T: int, H: int, grid_w: int, pool_h: int, pool_w: in
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     _check(load().draft_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _dt(q), heads, T, H, grid_w, d, pool_h, pool_w,
                                  _ptr(kv_idx), _ptr(kv_cnt), kv_idx.shape[-1], scale, _stream(stream)))
+    return out
+
+
+# --------------------------------------------------------------------------
+# FP8 (E4M3) variant
+# --------------------------------------------------------------------------
+def fp8_pitch(n: int) -> int:
+    """Row pitch (bytes) of a transposed code tensor: n rounded up to 16."""
+    return (n + 15) // 16 * 16
+
+
+def quantize_fp8_e4m3(x, transpose: bool = False, ld: int | None = None, out=None, scales=None, stream=None):
+    """Per-head E4M3 codes of x [heads, n, d] (bf16 or fp32). Returns (codes, scales):
+    codes uint8 [heads, n, d], or [heads, d, ld] when transpose (ld defaults to
+    fp8_pitch(n)); scales fp32 [heads] (the value of a code is decode(code) * scale)."""
+    torch = _torch()
+    heads, n, d = x.shape
+    if transpose:
+        ld = fp8_pitch(n) if ld is None else ld
+        shape = (heads, d, ld)
+    else:
+        ld = 0
+        shape = (heads, n, d)
+    if out is None:
+        out = torch.empty(shape, dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((heads,), dtype=torch.float32, device=x.device)
+    _contig_cuda(x, out, scales)
+    _check(load().quantize_fp8_e4m3(_ptr(x), _dt(x), heads, n, d, int(transpose), ld, _ptr(out), _ptr(scales),
+                                    _stream(stream)))
+    return out, scales
+
+
+def quantize_qkv_fp8(q, k, v, stream=None) -> dict:
+    """Codes and scales the FP8 attention takes: q8, k8 row-major, vt8 transposed."""
+    q8, qs = quantize_fp8_e4m3(q, stream=stream)
+    k8, ks = quantize_fp8_e4m3(k, stream=stream)
+    vt8, vs = quantize_fp8_e4m3(v, transpose=True, stream=stream)
+    return {"q8": q8, "k8": k8, "vt8": vt8, "q_scale": qs, "k_scale": ks, "v_scale": vs}
+
+
+def block_sparse_attn_fwd_fp8(q8, k8, vt8, q_scale, k_scale, v_scale, block_q: int, block_k: int, kv_idx, kv_cnt,
+                              mask_heads: int = 1, scale: float | None = None, out=None, stream=None):
+    """Block-sparse attention on E4M3 codes (vt8 [heads, 128, ldv]); returns O fp32 [heads, n, 128]."""
+    torch = _torch()
+    heads, n, d = q8.shape
+    if out is None:
+        out = torch.empty((heads, n, d), dtype=torch.float32, device=q8.device)
+    _contig_cuda(q8, k8, vt8, q_scale, k_scale, v_scale, out, kv_idx, kv_cnt)
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    _check(load().block_sparse_attn_fwd_fp8(_ptr(q8), _ptr(k8), _ptr(vt8), vt8.shape[-1], _ptr(q_scale),
+                                            _ptr(k_scale), _ptr(v_scale), _ptr(out), heads, n, d, block_q, block_k,
+                                            _ptr(kv_idx), _ptr(kv_cnt), kv_idx.shape[-1], mask_heads, scale,
+                                            _stream(stream)))
+    return out
+
+
+def dense_attn_fwd_fp8(q8, k8, vt8, q_scale, k_scale, v_scale, scale: float | None = None, out=None, stream=None):
+    """Dense attention on E4M3 codes; returns O fp32 [heads, n, 128]."""
+    torch = _torch()
+    heads, n, d = q8.shape
+    if out is None:
+        out = torch.empty((heads, n, d), dtype=torch.float32, device=q8.device)
+    _contig_cuda(q8, k8, vt8, q_scale, k_scale, v_scale, out)
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    _check(load().dense_attn_fwd_fp8(_ptr(q8), _ptr(k8), _ptr(vt8), vt8.shape[-1], _ptr(q_scale), _ptr(k_scale),
+                                     _ptr(v_scale), _ptr(out), heads, n, d, scale, _stream(stream)))
     return out

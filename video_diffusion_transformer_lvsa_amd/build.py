@@ -28,6 +28,8 @@ SOURCES = {
     "attn_f32.hip": [],
     "lvsa_mask.hip": [],
     "draft.hip": ["-ffp-contract=off"],
+    "fp8.hip": [],
+    "attn_fp8.hip": [],
 }
 
 COMMON = [

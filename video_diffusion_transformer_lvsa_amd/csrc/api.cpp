@@ -159,6 +159,38 @@ int run_attn(lvsa::AttnArgs& a, int dt, int d, void* stream) {
   return launched(e, "attention launch");
 }
 
+int check_fp8_attn(const void* q8, const void* k8, const void* vt8, int ldv, const float* qs, const float* ks,
+                   const float* vs, const float* o, int heads, int n, int d, float scale) {
+  if (d != 128) return fail(LVSA_EUNSUPPORTED, "FP8 attention supports d = 128 (got %d)", d);
+  if (heads < 0 || n < 0) return fail(LVSA_EINVAL, "heads=%d n=%d must be >= 0", heads, n);
+  if (n % 4 != 0) return fail(LVSA_EUNSUPPORTED, "FP8 attention needs n a multiple of 4 (got %d)", n);
+  if ((long long)n * d >= (1ll << 30)) return fail(LVSA_EINVAL, "n*d=%lld exceeds 2^30", (long long)n * d);
+  if (ldv < n || ldv % 16 != 0) return fail(LVSA_EINVAL, "ldv=%d must be a multiple of 16 and >= n=%d", ldv, n);
+  if ((long long)d * ldv >= (1ll << 31)) return fail(LVSA_EINVAL, "d*ldv exceeds 2^31");
+  if (!std::isfinite(scale)) return fail(LVSA_EINVAL, "scale must be finite");
+  if (heads > 0 && n > 0) {
+    if (!q8 || !k8 || !vt8 || !o || !qs || !ks || !vs)
+      return fail(LVSA_EINVAL, "q8, k8, vt8, o and the scales must be non-NULL");
+    if (!aligned16(q8) || !aligned16(k8) || !aligned16(vt8) || !aligned16(o))
+      return fail(LVSA_EINVAL, "q8, k8, vt8, o must be 16-byte aligned");
+    if ((reinterpret_cast<uintptr_t>(qs) | reinterpret_cast<uintptr_t>(ks) | reinterpret_cast<uintptr_t>(vs)) & 3u)
+      return fail(LVSA_EINVAL, "scales must be 4-byte aligned");
+  }
+  return LVSA_OK;
+}
+
+int run_fp8(lvsa::AttnArgs& a, const float* qs, const float* ks, const float* vs, void* stream) {
+  a.tiles_per_qb = (a.block_q + lvsa::kBM_BF16 - 1) / lvsa::kBM_BF16;
+  const long long total = (long long)a.heads * a.nqb * a.tiles_per_qb;
+  if (total >= (1ll << 31)) return fail(LVSA_EINVAL, "too many query tiles (%lld)", total);
+  a.total_tiles = (int)total;
+  if (total == 0) return LVSA_OK;
+  int rc = check_device();
+  if (rc) return rc;
+  return launched(lvsa::launch_attn_fp8(a, qs, ks, vs, reinterpret_cast<hipStream_t>(stream)),
+                  "FP8 attention launch");
+}
+
 }  // namespace
 
 extern "C" {
@@ -423,6 +455,96 @@ int dense_attn_fwd(const void* q, const void* k, const void* v, float* o, int dt
   a.scale_log2 = scale * 1.4426950408889634f;
   a.dense = 1;
   return run_attn(a, dt, d, stream);
+}
+
+int quantize_fp8_e4m3(const void* src, int dt, int heads, int n, int d, int transpose, int ld, uint8_t* dst,
+                      float* scales, void* stream) {
+  clear_err();
+  if (dt != LVSA_F32 && dt != LVSA_BF16) return fail(LVSA_EINVAL, "dtype %d unknown", dt);
+  if (d != 64 && d != 128) return fail(LVSA_EUNSUPPORTED, "head dim d=%d (supported: 64, 128)", d);
+  if (heads < 0 || n < 0) return fail(LVSA_EINVAL, "heads=%d n=%d must be >= 0", heads, n);
+  if ((long long)n * d >= (1ll << 30)) return fail(LVSA_EINVAL, "n*d=%lld exceeds 2^30", (long long)n * d);
+  if (transpose != 0 && transpose != 1) return fail(LVSA_EINVAL, "transpose=%d must be 0 or 1", transpose);
+  if (transpose) {
+    if (ld < n || ld % 16 != 0) return fail(LVSA_EINVAL, "ld=%d must be a multiple of 16 and >= n=%d", ld, n);
+    if ((long long)d * ld >= (1ll << 31)) return fail(LVSA_EINVAL, "d*ld exceeds 2^31");
+  } else if (ld != 0) {
+    return fail(LVSA_EINVAL, "ld=%d must be 0 when transpose = 0", ld);
+  }
+  if (heads == 0) return LVSA_OK;
+  if (!scales || (n > 0 && (!src || !dst))) return fail(LVSA_EINVAL, "src, dst, scales must be non-NULL");
+  if ((n > 0 && (!aligned16(src) || !aligned16(dst))) || (reinterpret_cast<uintptr_t>(scales) & 3u))
+    return fail(LVSA_EINVAL, "src, dst must be 16-byte aligned and scales 4-byte aligned");
+  int rc = check_device();
+  if (rc) return rc;
+  return launched(lvsa::launch_quantize_fp8(src, dt, heads, n, d, transpose != 0, ld, dst, scales,
+                                            reinterpret_cast<hipStream_t>(stream)),
+                  "fp8 quantization launch");
+}
+
+int block_sparse_attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* vt8, int ldv,
+                              const float* q_scale, const float* k_scale, const float* v_scale, float* o, int heads,
+                              int n, int d, int block_q, int block_k, const int32_t* kv_idx, const int32_t* kv_cnt,
+                              int max_kv, int mask_heads, float scale, void* stream) {
+  clear_err();
+  int rc = check_fp8_attn(q8, k8, vt8, ldv, q_scale, k_scale, v_scale, o, heads, n, d, scale);
+  if (rc) return rc;
+  if (block_q < 1 || block_k < 1) return fail(LVSA_EINVAL, "block_q=%d block_k=%d must be >= 1", block_q, block_k);
+  if (block_k < 64 || block_k % 4 != 0)
+    return fail(LVSA_EUNSUPPORTED, "block_k=%d: the FP8 kernel needs block_k >= 64 and a multiple of 4", block_k);
+  if (max_kv < 0) return fail(LVSA_EINVAL, "max_kv=%d must be >= 0", max_kv);
+  if (mask_heads != 1 && mask_heads != heads) return fail(LVSA_EINVAL, "mask_heads=%d must be 1 or heads=%d", mask_heads, heads);
+  if (heads == 0 || n == 0) return LVSA_OK;
+  if (!kv_cnt || (max_kv > 0 && !kv_idx)) return fail(LVSA_EINVAL, "kv_cnt (and kv_idx when max_kv > 0) must be non-NULL");
+  const long long nqb = ((long long)n + block_q - 1) / block_q;
+  const long long nkb = ((long long)n + block_k - 1) / block_k;
+  if ((long long)nkb * block_k >= (1ll << 31) || (long long)max_kv * block_k >= (1ll << 31))
+    return fail(LVSA_EINVAL, "key list spans more than 2^31 rows");
+  lvsa::AttnArgs a{};
+  a.q = q8;
+  a.k = k8;
+  a.v = vt8;
+  a.o = o;
+  a.heads = heads;
+  a.n = n;
+  a.block_q = block_q;
+  a.block_k = block_k;
+  a.nqb = (int)nqb;
+  a.nkb = (int)nkb;
+  a.kv_idx = kv_idx;
+  a.kv_cnt = kv_cnt;
+  a.max_kv = max_kv;
+  a.mask_heads = mask_heads;
+  a.scale = scale;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.ldv = ldv;
+  return run_fp8(a, q_scale, k_scale, v_scale, stream);
+}
+
+int dense_attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* vt8, int ldv, const float* q_scale,
+                       const float* k_scale, const float* v_scale, float* o, int heads, int n, int d, float scale,
+                       void* stream) {
+  clear_err();
+  int rc = check_fp8_attn(q8, k8, vt8, ldv, q_scale, k_scale, v_scale, o, heads, n, d, scale);
+  if (rc) return rc;
+  if (heads == 0 || n == 0) return LVSA_OK;
+  lvsa::AttnArgs a{};
+  a.q = q8;
+  a.k = k8;
+  a.v = vt8;
+  a.o = o;
+  a.heads = heads;
+  a.n = n;
+  a.block_q = n;
+  a.block_k = n;
+  a.nqb = 1;
+  a.nkb = 1;
+  a.mask_heads = 1;
+  a.scale = scale;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.dense = 1;
+  a.ldv = ldv;
+  return run_fp8(a, q_scale, k_scale, v_scale, stream);
 }
 
 }  // extern "C"

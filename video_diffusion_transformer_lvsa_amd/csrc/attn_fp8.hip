@@ -1,0 +1,361 @@
+// Block-sparse / dense softmax attention forward with FP8 (OCP E4M3)
+// operands on the gfx950 matrix cores (v_mfma_f32_32x32x64_f8f6f4), fp32
+// accumulation and softmax, fp32 output.
+//
+// What it computes: the attention of "LVSA: Training-Free Sparse Attention
+// for Long Video Diffusion" (§1 problem statement, §2 complexity) over the
+// listed KV blocks, on per-head E4M3 codes of Q, K and V: with q = sq*Q8,
+// k = sk*K8, v = sv*V8 (codes decoded exactly), O = softmax(scale * q kᵀ) v.
+// The Draft Attention article names quantization as its next step.
+//
+// Design, as the bf16 kernel (one workgroup = 4 waves = 128 query rows, the
+// KV list walked as one virtual key sequence in 64-key tiles, one barrier per
+// tile, K two tiles and V one tile ahead, Sᵀ of tile i+1 on the matrix core
+// while tile i's softmax runs) with these differences:
+//  * operands are bytes: a K tile is 64 rows x 128 B, a Vᵀ tile (V is given
+//    transposed, [heads, d, ldv]) is 128 rows x 64 B, each 8 KB; both come
+//    from global memory into LDS with LDS-destination buffer loads (16 B per
+//    lane; 4 B per lane where a Vᵀ row spans two key runs or starts off a
+//    16-byte boundary). Keys come in groups of 4 that are valid or not as a
+//    whole (n and block_k are multiples of 4), so one flag per group masks
+//    the scores of a partial tile;
+//  * the 32x32x64 MFMA operand layout (checked on the GPU): lane l holds row
+//    (A) or column (B) l mod 32 and k = 32*(l/32) .. +31, one byte each;
+//    Sᵀ = K Qᵀ takes 2 k-steps over d = 128, Oᵀ += Vᵀ Pᵀ one k-step over
+//    the 64 keys of a tile;
+//  * probabilities are rounded to E4M3 (v_cvt_pk_fp8_f32, nearest even; they
+//    are <= 2^8 by the lazy reference max, inside the range); the accumulator
+//    layout gives lane l, for each 32-key block, keys 8j + 4*(l/32) + t, so
+//    one v_permlane32_swap hands each half-wave the bytes of its own block and
+//    the Pᵀ operand has keys in order;
+//  * the row sum adds the unrounded fp32 probabilities.
+#include "attn_tiles.h"
+
+namespace lvsa {
+namespace {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ i32x8 lds_read32(const unsigned char* base, unsigned off0, unsigned off1) {
+  const u32x4 a = *(const u32x4*)(base + off0);
+  const u32x4 b = *(const u32x4*)(base + off1);
+  i32x8 r;
+  r[0] = (int)a[0]; r[1] = (int)a[1]; r[2] = (int)a[2]; r[3] = (int)a[3];
+  r[4] = (int)b[0]; r[5] = (int)b[1]; r[6] = (int)b[2]; r[7] = (int)b[3];
+  return r;
+}
+
+__device__ __forceinline__ unsigned int pack4_fp8(float a, float b, float c, float d) {
+  unsigned int w = 0u;
+  w = (unsigned int)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)w, false);
+  w = (unsigned int)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, (int)w, true);
+  return w;
+}
+
+template <int MODE>
+__global__ __launch_bounds__(kThreads, 2) void bsa_fwd_fp8_kernel(AttnArgs a, const float* __restrict__ qsc,
+                                                                  const float* __restrict__ ksc,
+                                                                  const float* __restrict__ vsc) {
+  constexpr int D = 128, BN = 64, NKB = 2, NDB = 4;
+  constexpr int TILE = BN * D;  // 8 KB per K or Vᵀ tile
+  __shared__ __attribute__((aligned(1024))) unsigned char ks0[TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char ks1[TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char vs0[TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char vs1[TILE];
+  __shared__ unsigned int kval[2][BN / 4];
+  auto kbuf = [&](int st) -> unsigned char* { return st == 0 ? ks0 : ks1; };
+  auto vbuf = [&](int st) -> unsigned char* { return st == 0 ? vs0 : vs1; };
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = lane >> 5;
+  const int l32 = lane & 31;
+
+  const int G = a.total_tiles;
+  const int w = blockIdx.x;
+  const int xcd = w & 7, idx = w >> 3, q8 = G >> 3, r8 = G & 7;
+  const int logical = (xcd < r8 ? xcd * (q8 + 1) : r8 * (q8 + 1) + (xcd - r8) * q8) + idx;
+  const int qt = logical % a.tiles_per_qb;
+  const int rest = logical / a.tiles_per_qb;
+  const int qb = rest % a.nqb;
+  const int h = rest / a.nqb;
+
+  const int blk_lo = qb * a.block_q;
+  const int blk_end = min(blk_lo + a.block_q, a.n);
+  const int row_lo = blk_lo + qt * kBM;
+  const int qrow = row_lo + wave * 32 + l32;
+  const bool q_valid = qrow < blk_end;
+
+  const size_t head_off = (size_t)h * (size_t)a.n * D;  // bytes: one byte per element
+  const int head_bytes = a.n * D;
+  const __amdgpu_buffer_rsrc_t Qr =
+      __builtin_amdgcn_make_buffer_rsrc((void*)((const uint8_t*)a.q + head_off), (short)0, head_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t Kr =
+      __builtin_amdgcn_make_buffer_rsrc((void*)((const uint8_t*)a.k + head_off), (short)0, head_bytes, 0x00020000);
+  const size_t vhead_off = (size_t)h * D * (size_t)a.ldv;  // Vᵀ rows have a.ldv bytes
+  const __amdgpu_buffer_rsrc_t Vr = __builtin_amdgcn_make_buffer_rsrc((void*)((const uint8_t*)a.v + vhead_off),
+                                                                      (short)0, D * a.ldv, 0x00020000);
+  float* __restrict__ Oh = a.o + head_off;
+
+  const int32_t* list = nullptr;
+  int cnt = 0, L = a.n;
+  if (MODE != MODE_DENSE) {
+    const int hm = a.mask_heads > 1 ? h : 0;
+    const int base = hm * a.nqb + qb;
+    cnt = a.kv_cnt[base];
+    cnt = cnt < 0 ? 0 : (cnt > a.max_kv ? a.max_kv : cnt);
+    list = a.kv_idx + (size_t)base * a.max_kv;
+    L = cnt * a.block_k;
+  }
+  if (row_lo >= blk_end) L = 0;
+  const int ntiles = (L + BN - 1) / BN;
+
+  // Qᵀ operand: lane (query l32, half) holds d = 64 s + 32 half .. +31.
+  i32x8 qreg[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const unsigned off = q_valid ? (unsigned)(qrow * D + 64 * s + 32 * half) : kInvalid;
+    const u32x4 lo = bload(Qr, off);
+    const u32x4 hi = bload(Qr, q_valid ? off + 16u : kInvalid);
+    qreg[s][0] = (int)lo[0]; qreg[s][1] = (int)lo[1]; qreg[s][2] = (int)lo[2]; qreg[s][3] = (int)lo[3];
+    qreg[s][4] = (int)hi[0]; qreg[s][5] = (int)hi[1]; qreg[s][6] = (int)hi[2]; qreg[s][7] = (int)hi[3];
+  }
+
+  // LDS layouts. K: row r (key) is 128 B, chunk c (16 B) at c ^ ((r >> 1) & 7).
+  // Vᵀ: row d is 64 B (keys), chunk c at c ^ ((d >> 2) & 3). Every 16-lane
+  // group of a 128-bit read then covers 16 distinct 16-byte bank groups.
+  // K loads: instruction j (0, 1) of wave `wave` fills rows 8(4j + wave) .. +7;
+  // lane: row + lane/8, LDS chunk lane%8.
+  // Tile row R = 8(4j + wave) + lane/8 has (R >> 1) & 7 = 4*(wave & 1) + lane/16.
+  const int kr_l = lane >> 3, kc_l = lane & 7;
+  const unsigned kdma = (unsigned)(kr_l * 128 + 16 * (kc_l ^ ((4 * (wave & 1) + (kr_l >> 1)) & 7)));
+  // Vᵀ loads (16 B): instruction j of wave `wave` fills rows d = 16(4j + wave) + lane/4, LDS chunk lane%4.
+  const int vd_l = lane >> 2, vc_l = lane & 3;
+  const unsigned vdma = (unsigned)(vd_l * a.ldv + 16 * (vc_l ^ ((vd_l >> 2) & 3)));
+
+  unsigned kra[2][2];  // [k-step][16-byte half of the 32-byte operand] for key row l32 (+32 kb)
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int c = 4 * s + 2 * half + u;
+      kra[s][u] = (unsigned)(l32 * 128 + 16 * (c ^ ((l32 >> 1) & 7)));
+    }
+  unsigned vra[2];  // Vᵀ row d = 32 db + l32, keys 32 half .. +31
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int c = 2 * half + u;
+    vra[u] = (unsigned)(l32 * 64 + 16 * (c ^ ((l32 >> 2) & 3)));
+  }
+
+  auto simple = [&](const TileD& t) { return t.full && t.bnd >= BN; };
+  // 16-byte V pieces also need a 16-byte aligned first key (a.ldv is a multiple of 16).
+  auto simple_v = [&](const TileD& t) { return t.full && t.bnd >= BN && (t.base0 & 15) == 0; };
+  auto dma16 = [&](__amdgpu_buffer_rsrc_t r, unsigned char* dst, unsigned voff, unsigned soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, voff, soff, 0, 0);
+  };
+  auto dma4 = [&](__amdgpu_buffer_rsrc_t r, unsigned char* dst, unsigned voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 4, voff, 0u, 0, 0);
+  };
+  auto load_k = [&](const TileD& t, int st) {
+    unsigned char* kb = kbuf(st);
+    if (simple(t)) {
+      const unsigned so = (unsigned)(t.base0 * D);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) dma16(Kr, kb + 1024 * (4 * j + wave), kdma, so + 1024u * (4 * j + wave));
+    } else {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int R = 8 * (4 * j + wave) + kr_l;
+        const int p = tile_row<BN, MODE>(a, t, list, cnt, R);
+        const unsigned off = p >= 0 ? (unsigned)(p * 128 + 16 * (kc_l ^ ((R >> 1) & 7))) : kInvalid;
+        dma16(Kr, kb + 1024 * (4 * j + wave), off, 0u);
+      }
+    }
+  };
+  auto load_v = [&](const TileD& t, int st) {
+    unsigned char* vb = vbuf(st);
+    if (simple_v(t)) {
+      const unsigned so = (unsigned)t.base0;
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        dma16(Vr, vb + 1024 * (4 * j + wave), vdma, so + (unsigned)(16 * (4 * j + wave)) * (unsigned)a.ldv);
+    } else {
+      // 4-byte pieces: instruction j (0..7) fills rows d = 4(4j + wave) + lane/16;
+      // LDS piece lane%16 of the row holds keys 4q .. 4q+3 of the tile.
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int d = 4 * (4 * j + wave) + (lane >> 4);
+        const int p4 = lane & 15;
+        const int q = 4 * ((p4 >> 2) ^ ((d >> 2) & 3)) + (p4 & 3);
+        const int p = tile_row<BN, MODE>(a, t, list, cnt, 4 * q);
+        dma4(Vr, vb + 256 * (4 * j + wave), p >= 0 ? (unsigned)(d * a.ldv + p) : kInvalid);
+        if (j == 0 && wave == 0 && d == 0) kval[st][q] = p >= 0 ? 0x01010101u : 0u;
+      }
+    }
+  };
+  auto qk = [&](int st, f32x16 (&s)[NKB]) {
+    const f32x16 zero = {};
+    const unsigned char* kb = kbuf(st);
+#pragma unroll
+    for (int ss = 0; ss < 2; ++ss) {
+#pragma unroll
+      for (int kb2 = 0; kb2 < NKB; ++kb2) {
+        const i32x8 A = lds_read32(kb + kb2 * 4096, kra[ss][0], kra[ss][1]);
+        s[kb2] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, qreg[ss], ss == 0 ? zero : s[kb2], 0, 0, 0, 0,
+                                                                   0, 0);
+      }
+    }
+  };
+  auto wait_dma = [&]() { __builtin_amdgcn_s_waitcnt(0x0F70); };  // vmcnt(0)
+
+  f32x16 oacc[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[i][r] = 0.f;
+  float mc = -INFINITY;
+  float l_run = 0.f;
+  const float c = a.scale_log2 * qsc[h] * ksc[h];
+
+  f32x16 s[NKB], sn[NKB];
+  int full_cur = 1;
+  TileStream ks;
+  stream_init<BN, MODE>(ks, a, list, cnt, 0);
+  TileD tprev;
+  if (ntiles > 0) {
+    const TileD t0 = stream_tile<BN, MODE>(ks, a, L);
+    stream_next<BN, MODE>(ks, a, list, cnt);
+    const TileD t1 = stream_tile<BN, MODE>(ks, a, L);
+    stream_next<BN, MODE>(ks, a, list, cnt);
+    load_k(t0, 0);
+    load_v(t0, 0);
+    load_k(t1, 1);
+    full_cur = t0.full;
+    tprev = t1;
+  }
+  wait_dma();
+  __syncthreads();
+  if (ntiles > 0) qk(0, s);
+  __syncthreads();
+
+  auto step = [&](const int st, f32x16 (&cur)[NKB], f32x16 (&nxt)[NKB]) {
+    const TileD tk = stream_tile<BN, MODE>(ks, a, L);
+    stream_next<BN, MODE>(ks, a, list, cnt);
+    const TileD tv = tprev;
+    tprev = tk;
+    load_k(tk, st);
+    load_v(tv, st ^ 1);
+
+    if (!full_cur) {
+#pragma unroll
+      for (int kb2 = 0; kb2 < NKB; ++kb2)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const unsigned f4 = kval[st][(kb2 * 32 + 8 * g + 4 * half) >> 2];
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (((f4 >> (8 * i)) & 0xffu) == 0u) cur[kb2][4 * g + i] = -INFINITY;
+        }
+    }
+
+    qk(st ^ 1, nxt);
+
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb2 = 0; kb2 < NKB; ++kb2)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, cur[kb2][r]);
+    mx = half_max(mx) * c;
+    const bool need = mx > mc + kRescale;
+    const float mc_new = need ? mx : mc;
+    const float alpha = need ? __builtin_amdgcn_exp2f(mc - mc_new) : 1.f;
+    mc = mc_new;
+    l_run *= alpha;
+    const float nm = (mc == -INFINITY) ? 0.f : -mc;
+
+    // P in E4M3: w[kb][j] holds the 4 keys kb*32 + 8j + 4*half + (0..3).
+    unsigned int pw[NKB][4];
+#pragma unroll
+    for (int kb2 = 0; kb2 < NKB; ++kb2)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float p[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          p[t] = __builtin_amdgcn_exp2f(__builtin_fmaf(cur[kb2][4 * j + t], c, nm));
+          l_run += p[t];
+        }
+        pw[kb2][j] = pack4_fp8(p[0], p[1], p[2], p[3]);
+      }
+    // Each half-wave keeps the words of its own 32-key block (X) and swaps the
+    // other block's words (Y) with the other half; the Pᵀ operand of half h
+    // then holds keys 32h .. 32h+31 in order.
+    i32x8 pB;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const unsigned int x = half ? pw[1][j] : pw[0][j];
+      const unsigned int y = half ? pw[0][j] : pw[1][j];
+      // sw[0] is the lower half's y, sw[1] the upper half's, in every lane.
+      auto sw = __builtin_amdgcn_permlane32_swap(y, y, false, false);
+      const unsigned int yo = half ? sw[0] : sw[1];
+      pB[2 * j] = (int)(half ? yo : x);
+      pB[2 * j + 1] = (int)(half ? x : yo);
+    }
+
+    if (__ballot(need && (l_run == l_run)) != 0ull) {
+#pragma unroll
+      for (int i = 0; i < NDB; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
+    }
+
+    const unsigned char* vb = vbuf(st);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const i32x8 A = lds_read32(vb + db * 2048, vra[0], vra[1]);
+      oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, pB, oacc[db], 0, 0, 0, 0, 0, 0);
+    }
+
+    full_cur = tv.full;
+    wait_dma();
+    __syncthreads();
+  };
+
+  int it = 0;
+  for (; it + 1 < ntiles; it += 2) {
+    step(0, s, sn);
+    step(1, sn, s);
+  }
+  if (it < ntiles) step(0, s, sn);
+
+  const float l_tot = half_sum(l_run);
+  const float inv = l_tot > 0.f ? vsc[h] / l_tot : 0.f;
+  if (q_valid) {
+    float* orow = Oh + (size_t)qrow * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = 32 * db + 8 * g + 4 * half;
+        *(float4*)(orow + d0) = make_float4(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv,
+                                            oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
+      }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attn_fp8(const AttnArgs& a, const float* qs, const float* ks, const float* vs, hipStream_t s) {
+  if (a.total_tiles == 0) return hipSuccess;
+  dim3 grid(a.total_tiles), block(kThreads);
+  if (a.dense)
+    hipLaunchKernelGGL(bsa_fwd_fp8_kernel<MODE_DENSE>, grid, block, 0, s, a, qs, ks, vs);
+  else
+    hipLaunchKernelGGL(bsa_fwd_fp8_kernel<MODE_LIST>, grid, block, 0, s, a, qs, ks, vs);
+  return hipGetLastError();
+}
+
+}  // namespace lvsa

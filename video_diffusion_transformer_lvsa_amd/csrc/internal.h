@@ -39,6 +39,7 @@ struct AttnArgs {
   int rpt;  // tile rows per 64-slot key tile (64 / pw)
   int lpw;  // log2(pw): pw divides 64
   float inv_per, inv_nbw;  // 1 / (nbh * nbw), 1 / nbw: block index -> (t, hb, wb)
+  int ldv;                 // FP8 kernel: row pitch in bytes of the transposed V, [heads, d, ldv]
 };
 
 // Query rows per workgroup of the bf16 MFMA kernel and of the fp32 kernel.
@@ -49,6 +50,9 @@ hipError_t launch_attn_bf16(const AttnArgs& a, int d, hipStream_t s);
 // Draft attention on the raster layout (d = 128, bf16): a.tile2d = 1.
 hipError_t launch_draft_attn_bf16(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_f32(const AttnArgs& a, int d, hipStream_t s);
+// E4M3 codes (q, k row-major [heads, n, 128], v transposed [heads, 128, a.ldv])
+// with per-head dequantization factors qs, ks, vs (device arrays).
+hipError_t launch_attn_fp8(const AttnArgs& a, const float* qs, const float* ks, const float* vs, hipStream_t s);
 
 hipError_t launch_lvsa_mask(int T, int C, int window, int T_per, int step, int32_t* kv_idx, int32_t* kv_cnt,
                             int cap, hipStream_t s);
@@ -72,6 +76,11 @@ hipError_t launch_draft_select(const float* qbar, const float* kbarT, int heads,
                                int32_t* kv_idx, int32_t* kv_cnt, hipStream_t s);
 hipError_t launch_draft_scores(const float* qbar, const float* kbar, int heads, int nb_q, int nb_k, int d,
                                float* scores, hipStream_t s);
+// Per-head E4M3 codes of src ([heads, n, d], dtype 0 = f32, 1 = bf16) into dst
+// ([heads, n, d], or [heads, d, ld] when transpose: d <= 128, ld a multiple of
+// 16, >= n); scales[h] receives the dequantization factor.
+hipError_t launch_quantize_fp8(const void* src, int dt, int heads, int n, int d, bool transpose, int ld,
+                               uint8_t* dst, float* scales, hipStream_t s);
 hipError_t launch_token_permute(const void* src, void* dst, int esize, int heads, int n_src, int n_dst, int d,
                                 const int32_t* map, hipStream_t s);
 
