@@ -494,7 +494,11 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_d128_kernel(AttnArgs a) {
 
   // A tile whose 64 rows are valid and are 4 runs of 16 consecutive rows of
   // K/V (one run per DMA instruction) loads with one scalar offset per run.
-  auto simple = [&](const TileD& t) { return MODE == MODE_T2D ? (t.full && a.pw == 16) : (t.full && t.bnd >= BN); };
+  // All BN rows valid and physically consecutive from base0: one run, or two
+  // runs of adjacent blocks (then base1 == base0).
+  auto simple = [&](const TileD& t) {
+    return MODE == MODE_T2D ? (t.full && a.pw == 16) : (t.full && (t.bnd >= BN || t.base1 == t.base0));
+  };
   const unsigned run_bytes = MODE == MODE_T2D ? (unsigned)a.gW * D * 2 : 4096u;
   auto dma = [&](__amdgpu_buffer_rsrc_t r, int st, int kind, int j, unsigned voff, unsigned soff) {
     unsigned char* dst = (kind == 0 ? kbuf(st) : vbuf(st)) + 4096 * j + 1024 * wave;

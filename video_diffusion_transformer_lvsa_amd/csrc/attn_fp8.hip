@@ -15,8 +15,8 @@
 //  * operands are bytes: a K tile is 64 rows x 128 B, a Vᵀ tile (V is given
 //    transposed, [heads, d, ldv]) is 128 rows x 64 B, each 8 KB; both come
 //    from global memory into LDS with LDS-destination buffer loads (16 B per
-//    lane; 4 B per lane where a Vᵀ row spans two key runs or starts off a
-//    16-byte boundary). Keys come in groups of 4 that are valid or not as a
+//    lane; 4 B per lane where a Vᵀ row spans two runs that are not
+//    adjacent). Keys come in groups of 4 that are valid or not as a
 //    whole (n and block_k are multiples of 4), so one flag per group masks
 //    the scores of a partial tile;
 //  * the 32x32x64 MFMA operand layout (checked on the GPU): lane l holds row
@@ -24,10 +24,12 @@
 //    Sᵀ = K Qᵀ takes 2 k-steps over d = 128, Oᵀ += Vᵀ Pᵀ one k-step over
 //    the 64 keys of a tile;
 //  * probabilities are rounded to E4M3 (v_cvt_pk_fp8_f32, nearest even; they
-//    are <= 2^8 by the lazy reference max, inside the range); the accumulator
-//    layout gives lane l, for each 32-key block, keys 8j + 4*(l/32) + t, so
-//    one v_permlane32_swap hands each half-wave the bytes of its own block and
-//    the Pᵀ operand has keys in order;
+//    are <= 2^8 by the lazy reference max, inside the range). K rows sit in
+//    LDS in a permuted order, row r = 32kb + 8g + 4h + i holding key
+//    32h + 16kb + 4g + i, so that the Sᵀ accumulator of lane (query, half h)
+//    holds exactly keys 32h .. 32h+31, in the byte order of the PV product's
+//    B operand: the packed probabilities feed the matrix core as they are,
+//    with no exchange between the half-waves;
 //  * the row sum adds the unrounded fp32 probabilities.
 #include "attn_tiles.h"
 
@@ -51,6 +53,11 @@ __device__ __forceinline__ unsigned int pack4_fp8(float a, float b, float c, flo
   w = (unsigned int)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)w, false);
   w = (unsigned int)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, (int)w, true);
   return w;
+}
+
+// Tile key held by K row r of LDS: r = 32kb + 8g + 4h + i -> 32h + 16kb + 4g + i.
+__device__ __forceinline__ int krow(int r) {
+  return (((r >> 2) & 1) << 5) | (((r >> 5) & 1) << 4) | (((r >> 3) & 3) << 2) | (r & 3);
 }
 
 template <int MODE>
@@ -126,11 +133,15 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_fp8_kernel(AttnArgs a, co
   // LDS layouts. K: row r (key) is 128 B, chunk c (16 B) at c ^ ((r >> 1) & 7).
   // Vᵀ: row d is 64 B (keys), chunk c at c ^ ((d >> 2) & 3). Every 16-lane
   // group of a 128-bit read then covers 16 distinct 16-byte bank groups.
-  // K loads: instruction j (0, 1) of wave `wave` fills rows 8(4j + wave) .. +7;
-  // lane: row + lane/8, LDS chunk lane%8.
-  // Tile row R = 8(4j + wave) + lane/8 has (R >> 1) & 7 = 4*(wave & 1) + lane/16.
+  // K loads: instruction j (0, 1) of wave `wave` fills LDS rows R = 8(4j + wave)
+  // + lane/8, LDS chunk lane%8, from tile key krow(R).
   const int kr_l = lane >> 3, kc_l = lane & 7;
-  const unsigned kdma = (unsigned)(kr_l * 128 + 16 * (kc_l ^ ((4 * (wave & 1) + (kr_l >> 1)) & 7)));
+  unsigned kdma[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int R = 8 * (4 * j + wave) + kr_l;
+    kdma[j] = (unsigned)(krow(R) * 128 + 16 * (kc_l ^ ((R >> 1) & 7)));
+  }
   // Vᵀ loads (16 B): instruction j of wave `wave` fills rows d = 16(4j + wave) + lane/4, LDS chunk lane%4.
   const int vd_l = lane >> 2, vc_l = lane & 3;
   const unsigned vdma = (unsigned)(vd_l * a.ldv + 16 * (vc_l ^ ((vd_l >> 2) & 3)));
@@ -150,9 +161,11 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_fp8_kernel(AttnArgs a, co
     vra[u] = (unsigned)(l32 * 64 + 16 * (c ^ ((l32 >> 2) & 3)));
   }
 
-  auto simple = [&](const TileD& t) { return t.full && t.bnd >= BN; };
-  // 16-byte V pieces also need a 16-byte aligned first key (a.ldv is a multiple of 16).
-  auto simple_v = [&](const TileD& t) { return t.full && t.bnd >= BN && (t.base0 & 15) == 0; };
+  // All BN rows valid and physically consecutive from base0: one run, or two
+  // runs of adjacent blocks (then base1 == base0). The 16-byte V pieces of
+  // such a tile start at any multiple of 4 bytes (base0 and a.ldv are), which
+  // the LDS-destination loads accept.
+  auto simple = [&](const TileD& t) { return t.full && (t.bnd >= BN || t.base1 == t.base0); };
   auto dma16 = [&](__amdgpu_buffer_rsrc_t r, unsigned char* dst, unsigned voff, unsigned soff) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, voff, soff, 0, 0);
   };
@@ -164,12 +177,12 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_fp8_kernel(AttnArgs a, co
     if (simple(t)) {
       const unsigned so = (unsigned)(t.base0 * D);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) dma16(Kr, kb + 1024 * (4 * j + wave), kdma, so + 1024u * (4 * j + wave));
+      for (int j = 0; j < 2; ++j) dma16(Kr, kb + 1024 * (4 * j + wave), kdma[j], so);
     } else {
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int R = 8 * (4 * j + wave) + kr_l;
-        const int p = tile_row<BN, MODE>(a, t, list, cnt, R);
+        const int p = tile_row<BN, MODE>(a, t, list, cnt, krow(R));
         const unsigned off = p >= 0 ? (unsigned)(p * 128 + 16 * (kc_l ^ ((R >> 1) & 7))) : kInvalid;
         dma16(Kr, kb + 1024 * (4 * j + wave), off, 0u);
       }
@@ -177,7 +190,7 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_fp8_kernel(AttnArgs a, co
   };
   auto load_v = [&](const TileD& t, int st) {
     unsigned char* vb = vbuf(st);
-    if (simple_v(t)) {
+    if (simple(t)) {
       const unsigned so = (unsigned)t.base0;
 #pragma unroll
       for (int j = 0; j < 2; ++j)
@@ -254,7 +267,8 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_fp8_kernel(AttnArgs a, co
       for (int kb2 = 0; kb2 < NKB; ++kb2)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const unsigned f4 = kval[st][(kb2 * 32 + 8 * g + 4 * half) >> 2];
+          // score rows 32kb + 8g + 4h + i are keys 32h + 16kb + 4g + i
+          const unsigned f4 = kval[st][8 * half + 4 * kb2 + g];
 #pragma unroll
           for (int i = 0; i < 4; ++i)
             if (((f4 >> (8 * i)) & 0xffu) == 0u) cur[kb2][4 * g + i] = -INFINITY;
@@ -276,34 +290,22 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_fp8_kernel(AttnArgs a, co
     l_run *= alpha;
     const float nm = (mc == -INFINITY) ? 0.f : -mc;
 
-    // P in E4M3: w[kb][j] holds the 4 keys kb*32 + 8j + 4*half + (0..3).
-    unsigned int pw[NKB][4];
+    // P in E4M3: word 4kb + g of the Pᵀ operand holds the scores
+    // cur[kb][4g .. 4g+3], keys 32*half + 16kb + 4g + (0..3): byte k of the
+    // operand is key 32*half + k.
+    i32x8 pB;
 #pragma unroll
     for (int kb2 = 0; kb2 < NKB; ++kb2)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int g = 0; g < 4; ++g) {
         float p[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          p[t] = __builtin_amdgcn_exp2f(__builtin_fmaf(cur[kb2][4 * j + t], c, nm));
+          p[t] = __builtin_amdgcn_exp2f(__builtin_fmaf(cur[kb2][4 * g + t], c, nm));
           l_run += p[t];
         }
-        pw[kb2][j] = pack4_fp8(p[0], p[1], p[2], p[3]);
+        pB[4 * kb2 + g] = (int)pack4_fp8(p[0], p[1], p[2], p[3]);
       }
-    // Each half-wave keeps the words of its own 32-key block (X) and swaps the
-    // other block's words (Y) with the other half; the Pᵀ operand of half h
-    // then holds keys 32h .. 32h+31 in order.
-    i32x8 pB;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const unsigned int x = half ? pw[1][j] : pw[0][j];
-      const unsigned int y = half ? pw[0][j] : pw[1][j];
-      // sw[0] is the lower half's y, sw[1] the upper half's, in every lane.
-      auto sw = __builtin_amdgcn_permlane32_swap(y, y, false, false);
-      const unsigned int yo = half ? sw[0] : sw[1];
-      pB[2 * j] = (int)(half ? yo : x);
-      pB[2 * j + 1] = (int)(half ? x : yo);
-    }
 
     if (__ballot(need && (l_run == l_run)) != 0ull) {
 #pragma unroll
