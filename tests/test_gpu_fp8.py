@@ -181,7 +181,7 @@ def _assert_within_bound(got, ref, bound, model, vmax, what, slack=None):
     return m, r, worst
 
 
-DENSE_N = [4, 64, 1000, 4100]
+DENSE_N = [4, 64, 1000, 4100, 1200]  # 1000 and 1200 (n mod 256 > 128) run 8-wave workgroups
 
 
 def _integer_v(rng, heads, n, d):
@@ -208,10 +208,13 @@ def test_fp8_dense_k_zero_is_mean_of_v(n):
 
 
 LVSA_FP8 = [
-    # T, H, W, heads, C, window, T_per   (P = H*W: 64, 100, 1560; multiples of 4)
+    # T, H, W, heads, C, window, T_per   (P = H*W, multiples of 4: 64, 100, 1560 run
+    # 4-wave workgroups (128 query rows); 256 and 200 run 8-wave ones (256 rows))
     (6, 8, 8, 2, 3, 2, 2),
     (5, 10, 10, 2, 3, 2, 3),
     (12, 30, 52, 2, 5, 3, 4),
+    (6, 16, 16, 2, 3, 2, 2),
+    (5, 10, 20, 2, 3, 2, 3),
 ]
 
 

@@ -180,7 +180,8 @@ int check_fp8_attn(const void* q8, const void* k8, const void* vt8, int ldv, con
 }
 
 int run_fp8(lvsa::AttnArgs& a, const float* qs, const float* ks, const float* vs, void* stream) {
-  a.tiles_per_qb = (a.block_q + lvsa::kBM_BF16 - 1) / lvsa::kBM_BF16;
+  const int bm = lvsa::fp8_rows_per_workgroup(a);
+  a.tiles_per_qb = (a.block_q + bm - 1) / bm;
   const long long total = (long long)a.heads * a.nqb * a.tiles_per_qb;
   if (total >= (1ll << 31)) return fail(LVSA_EINVAL, "too many query tiles (%lld)", total);
   a.total_tiles = (int)total;
