@@ -261,7 +261,7 @@ def run_lvsa(args, w):
         "unit": "TFLOP/s",
         "frac": round(achieved / peak, 4),
         "traffic": traffic_for(w.name + ("-fp8" if fp8 else ""), ATTN_FP8_SRC if fp8 else ATTN_SRC),
-        "kernel": "bsa_fwd_fp8_kernel<MODE_LIST>" if fp8 else "bsa_fwd_d128_kernel<MODE_LIST, false>",
+        "kernel": "bsa_fwd_fp8_kernel<MODE_LIST, 4>" if fp8 else "bsa_fwd_d128_kernel<MODE_LIST, false>",
     }
 
     if not args.no_dense:
