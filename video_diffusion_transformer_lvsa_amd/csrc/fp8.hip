@@ -41,14 +41,27 @@ __device__ __forceinline__ void load8(const void* src, size_t e, bool bf16, floa
 }
 
 // amax[h] = max |x| over head h (as float bits: non-negative floats order as
-// unsigned integers). Grid: (blocks per head, heads).
+// unsigned integers). Four 8-element loads in flight per thread, one atomic
+// per workgroup. Grid: (blocks per head, heads).
 template <bool BF16>
 __global__ __launch_bounds__(256) void amax_kernel(const void* __restrict__ src, int per_head,
                                                    float* __restrict__ amax) {
+  __shared__ float wmax[4];
   const int h = blockIdx.y;
   const size_t base = (size_t)h * per_head;
+  const int stride = gridDim.x * 256 * 8;
   float m = 0.f;
-  for (int e = (blockIdx.x * 256 + threadIdx.x) * 8; e < per_head; e += gridDim.x * 256 * 8) {
+  int e = (blockIdx.x * 256 + threadIdx.x) * 8;
+  for (; e + 3 * stride < per_head; e += 4 * stride) {
+    float x[4][8];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) load8(src, base + e + (size_t)u * stride, BF16, x[u]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(x[u][i]));
+  }
+  for (; e < per_head; e += stride) {
     float x[8];
     load8(src, base + e, BF16, x);
 #pragma unroll
@@ -56,7 +69,12 @@ __global__ __launch_bounds__(256) void amax_kernel(const void* __restrict__ src,
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-  if ((threadIdx.x & 63) == 0) atomicMax((unsigned int*)&amax[h], __float_as_uint(m));
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    m = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+    atomicMax((unsigned int*)&amax[h], __float_as_uint(m));
+  }
 }
 
 __device__ __forceinline__ float head_scale(float amax) { return amax > 0.f ? __fdiv_rn(amax, 448.f) : 1.f; }
