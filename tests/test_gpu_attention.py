@@ -127,6 +127,48 @@ def test_bf16_block_list_edge_cases():
     assert np.all(o[1, bq : 2 * bq] == 0)
 
 
+@pytest.mark.parametrize("n,bq,bk,max_kv,mask_heads,sorted_lists", [
+    (1000, 150, 96, 6, 2, False),   # 22-row last tiles; 7 blocks, the last one short
+    (1000, 150, 96, 6, 1, True),
+    (1100, 180, 64, 9, 2, False),   # 52-row last tiles
+    (640, 130, 64, 5, 2, False),    # 2-row last tiles
+    (1560 * 3, 1560, 1560, 3, 1, True),
+    (900, 300, 100, 200, 2, False),  # long lists
+])
+def test_bf16_ragged_query_blocks(n, bq, bk, max_kv, mask_heads, sorted_lists):
+    """Query blocks that end in a partial 128-row tile, with unsorted lists,
+    repeated entries (counted twice), entries outside [0, nkb), empty lists
+    and kv_cnt above max_kv."""
+    torch = _torch()
+    rng = np.random.default_rng(n + bq)
+    heads, d = 2, 128
+    q, k, v = (synth.bf16_round(rng.standard_normal((heads, n, d)).astype(np.float32) * sc) for sc in (1.5, 1.5, 1.0))
+    nqb, nkb = math.ceil(n / bq), math.ceil(n / bk)
+    hm = mask_heads
+    idx = rng.integers(-1, nkb + 1, size=(hm, nqb, max_kv)).astype(np.int32)
+    cnt = rng.integers(0, max_kv + 1, size=(hm, nqb)).astype(np.int32)
+    if sorted_lists:
+        idx = np.sort(rng.integers(0, nkb, size=(hm, nqb, max_kv)), axis=-1).astype(np.int32)
+    else:
+        idx[0, 0, : min(3, max_kv)] = idx[0, 0, 0]  # repeats
+    cnt[0, 1] = 0
+    cnt[-1, -1] = max_kv + 7
+    note(f"ragged query blocks n={n} bq={bq} bk={bk} max_kv={max_kv} mask_heads={hm}")
+    o = to_host(_lib.block_sparse_attn_fwd(to_dev(q), to_dev(k), to_dev(v), bq, bk, torch.from_numpy(idx).cuda(),
+                                           torch.from_numpy(cnt).cuda(), mask_heads=hm))
+    cnt_o = np.minimum(cnt, max_kv)
+    clean = np.zeros_like(idx)
+    ccnt = np.zeros_like(cnt_o)
+    for h in range(hm):
+        for b in range(nqb):
+            keep = [x for x in idx[h, b, : cnt_o[h, b]] if 0 <= x < nkb]
+            clean[h, b, : len(keep)] = keep
+            ccnt[h, b] = len(keep)
+    ref = oracle.block_sparse_attention(q, k, v, bq, bk, clean, ccnt, mask_heads=hm)
+    assert_attn_close(o, ref, what="ragged query blocks")
+    assert np.all(o[0, bq : 2 * bq] == 0)  # empty list of block 1 (head 0)
+
+
 def test_bf16_closed_forms():
     torch = _torch()
     rng = np.random.default_rng(12)
