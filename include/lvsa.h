@@ -230,17 +230,19 @@ int dense_attn_fwd(const void* q, const void* k, const void* v, float* o, int dt
  * transpose = 0: dst [heads, n, d], ld must be 0.
  * transpose = 1: dst [heads, d, ld], dst[h, c, i] = code of src[h, i, c];
  *   ld (row pitch in bytes) a multiple of 16 and >= n; bytes n .. ld-1 of a
- *   row are left as they are. This is the layout the attention takes V in.
+ *   row are set to 0. This is the layout the attention takes V in.
  * scales: device float[heads], written. d is 64 or 128; n*d < 2^30 and
  * d*ld < 2^31. src, dst 16-byte aligned; scales 4-byte aligned. */
 int quantize_fp8_e4m3(const void* src, int dt, int heads, int n, int d, int transpose, int ld, uint8_t* dst,
                       float* scales, void* stream);
 
 /* Block-sparse attention on E4M3 operands: q8, k8 [heads, n, 128] codes,
- * vt8 [heads, 128, ldv] codes of Vᵀ (quantize_fp8_e4m3 with transpose = 1),
- * q_scale, k_scale, v_scale device float[heads]. Same key lists, masking
- * and output layout as block_sparse_attn_fwd (block_valid is not taken),
- * on the values q = q_scale[h] * decode(q8) (likewise k, v):
+ * vt8 [heads, 128, ldv] codes of Vᵀ (quantize_fp8_e4m3 with transpose = 1;
+ * every byte of a row, padding included, must be a finite code, which the
+ * quantizer guarantees), q_scale, k_scale, v_scale device float[heads].
+ * Same key lists, block_valid, pad rows and output layout as
+ * block_sparse_attn_fwd (Draft: q8/k8/vt8 quantized from the reordered
+ * tensors), on the values q = q_scale[h] * decode(q8) (likewise k, v):
  *   s_ij = scale * <q_i, k_j> (exact products, fp32 sums, on the FP8
  *   matrix cores), probabilities exp(s_ij - m) in fp32 with m the running
  *   maximum (updated only when it grows by more than 2^8 in base 2), the
@@ -252,7 +254,18 @@ int quantize_fp8_e4m3(const void* src, int dt, int heads, int n, int d, int tran
 int block_sparse_attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* vt8, int ldv,
                               const float* q_scale, const float* k_scale, const float* v_scale, float* o, int heads,
                               int n, int d, int block_q, int block_k, const int32_t* kv_idx, const int32_t* kv_cnt,
-                              int max_kv, int mask_heads, float scale, void* stream);
+                              int max_kv, int mask_heads, const int32_t* block_valid, float scale, void* stream);
+
+/* FP8 Draft attention on the raster layout  [DRAFT, as draft_attn_fwd]:
+ * draft_attn_fwd's blocks, lists and output on E4M3 operands (q8, k8
+ * [heads, T*H*grid_w, 128], vt8 [heads, 128, ldv], per-head scales), with
+ * block_sparse_attn_fwd_fp8's arithmetic. Requires d = 128,
+ * pool_h*pool_w a multiple of 64, pool_w in {4, 8, 16, 32, 64} and grid_w a
+ * multiple of 4 (LVSA_EUNSUPPORTED otherwise). */
+int draft_attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* vt8, int ldv, const float* q_scale,
+                       const float* k_scale, const float* v_scale, float* o, int heads, int T, int H, int grid_w,
+                       int d, int pool_h, int pool_w, const int32_t* kv_idx, const int32_t* kv_cnt, int max_kv,
+                       float scale, void* stream);
 
 /* Dense FP8 attention: every query attends to all n keys; arithmetic and
  * layouts as block_sparse_attn_fwd_fp8 (d = 128, n a multiple of 4). */

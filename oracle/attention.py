@@ -120,7 +120,7 @@ def block_sparse_attention(q, k, v, block_q: int, block_k: int, kv_idx, kv_cnt, 
 
 
 def draft_attention_original_order(q, k, v, perm, inv_perm, block_valid, block_size: int, kv_idx, kv_cnt,
-                                   scale: float | None = None, heads=None, rows=None) -> np.ndarray:
+                                   scale: float | None = None, heads=None, rows=None, fn=None) -> np.ndarray:
     """Draft block-sparse attention computed directly in the original token order.
 
     Token n sits in block b = inv_perm[n] // block_size of the reorder; its keys
@@ -129,7 +129,9 @@ def draft_attention_original_order(q, k, v, perm, inv_perm, block_valid, block_s
     comparing this with reorder -> block-sparse attention -> inverse reorder
     checks that the reorder does not change the result.
     Returns fp64 [len(heads), len(rows), d] (rows = original token indices,
-    default all)."""
+    default all). fn evaluates a row set over its keys (default:
+    attention_keyset)."""
+    fn = attention_keyset if fn is None else fn
     H, n, d = q.shape
     scale = 1.0 / np.sqrt(d) if scale is None else scale
     heads = list(range(H)) if heads is None else list(heads)
@@ -143,5 +145,5 @@ def draft_attention_original_order(q, k, v, perm, inv_perm, block_valid, block_s
             keys = np.concatenate(
                 [perm[bb * block_size : bb * block_size + int(block_valid[bb])] for bb in kv_idx[h, b, : int(kv_cnt[h, b])]]
             )
-            out[hi, sel] = attention_keyset(to_f64(q[h, rows[sel]]), to_f64(k[h, keys]), to_f64(v[h, keys]), scale)
+            out[hi, sel] = fn(to_f64(q[h, rows[sel]]), to_f64(k[h, keys]), to_f64(v[h, keys]), scale)
     return out

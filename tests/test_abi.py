@@ -178,7 +178,8 @@ def test_fp8_validation(lib):
     assert qz(*empty) == 0
 
     bs = lib.block_sparse_attn_fwd_fp8
-    ok = [FAKE, FAKE, FAKE, 1568, FAKE, FAKE, FAKE, FAKE, 2, 1560, 128, 1560, 1560, FAKE, FAKE, 3, 1, 0.088, None]
+    ok = [FAKE, FAKE, FAKE, 1568, FAKE, FAKE, FAKE, FAKE, 2, 1560, 128, 1560, 1560, FAKE, FAKE, 3, 1, None, 0.088,
+          None]
     for i, val, code in [(10, 64, _lib.LVSA_EUNSUPPORTED),   # d
                          (9, 1558, _lib.LVSA_EUNSUPPORTED),  # n not a multiple of 4
                          (3, 1552, _lib.LVSA_EINVAL),        # ldv < n
@@ -188,16 +189,37 @@ def test_fp8_validation(lib):
                          (11, 0, _lib.LVSA_EINVAL),          # block_q
                          (16, 3, _lib.LVSA_EINVAL),          # mask_heads
                          (15, -1, _lib.LVSA_EINVAL),         # max_kv
-                         (17, float("nan"), _lib.LVSA_EINVAL),
+                         (18, float("nan"), _lib.LVSA_EINVAL),
                          (4, None, _lib.LVSA_EINVAL),        # q_scale
                          (0, MIS, _lib.LVSA_EINVAL),         # q8 misaligned
                          (14, None, _lib.LVSA_EINVAL)]:      # kv_cnt
         bad = list(ok)
         bad[i] = val
         assert bs(*bad) == code, (i, val)
+    bad = list(ok)
+    bad[11], bad[17] = 128, FAKE  # block_valid needs block_q == block_k
+    assert bs(*bad) == _lib.LVSA_EINVAL
     empty = list(ok)
     empty[8] = 0
     assert bs(*empty) == 0
+    da = lib.draft_attn_fwd_fp8
+    ok = [FAKE, FAKE, FAKE, 118800, FAKE, FAKE, FAKE, FAKE, 2, 33, 45, 80, 128, 8, 16, FAKE, FAKE, 99, 0.088, None]
+    for i, val, code in [(12, 64, _lib.LVSA_EUNSUPPORTED),   # d
+                         (11, 78, _lib.LVSA_EUNSUPPORTED),   # grid_w not a multiple of 4
+                         (14, 2, _lib.LVSA_EUNSUPPORTED),    # pool_w = 2 (pool 8x2 = 16 slots as well)
+                         (3, 118784, _lib.LVSA_EINVAL),      # ldv < n
+                         (17, -1, _lib.LVSA_EINVAL),         # max_kv
+                         (16, None, _lib.LVSA_EINVAL),       # kv_cnt
+                         (4, None, _lib.LVSA_EINVAL)]:       # q_scale
+        bad = list(ok)
+        bad[i] = val
+        assert da(*bad) == code, (i, val)
+    bad = list(ok)
+    bad[13], bad[14] = 32, 2  # 64 slots, but pool_w = 2
+    assert da(*bad) == _lib.LVSA_EUNSUPPORTED
+    empty = list(ok)
+    empty[8] = 0
+    assert da(*empty) == 0
     dn = lib.dense_attn_fwd_fp8
     ok = [FAKE, FAKE, FAKE, 1008, FAKE, FAKE, FAKE, FAKE, 2, 1000, 128, 0.088, None]
     assert dn(*(ok[:10] + [64] + ok[11:])) == _lib.LVSA_EUNSUPPORTED

@@ -361,3 +361,117 @@ def test_full_wan13b_6x_lvsa_fp8():
         del o
     del dev
     torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------------------
+# Draft Attention in FP8: the reorder path (block_valid) and the raster path
+# ---------------------------------------------------------------------------
+def _draft_fp8_both(q, k, v, T, H, W, ph, pw, sp):
+    """Mask from the bf16 inputs; FP8 attention on the reordered tensors
+    (scattered back) and on the raster layout. Returns (o_reorder, o_raster,
+    mask outputs)."""
+    torch = _torch()
+    heads = q.shape[0]
+    dq, dk, dv = to_dev(q), to_dev(k), to_dev(v)
+    out = _lib.draft_mask_and_perm(dq, dk, dv, T, H, W, ph, pw, sp)
+    bs = ph * pw
+    pq = _lib.quantize_qkv_fp8(out["q_perm"], out["k_perm"], out["v_perm"])
+    op = _lib.block_sparse_attn_fwd_fp8(pq["q8"], pq["k8"], pq["vt8"], pq["q_scale"], pq["k_scale"], pq["v_scale"],
+                                        bs, bs, out["kv_idx"], out["kv_cnt"], mask_heads=heads,
+                                        block_valid=out["block_valid"])
+    o = _lib.token_permute(op, out["inv_perm"])
+    rq = _lib.quantize_qkv_fp8(dq, dk, dv)
+    o2 = _lib.draft_attn_fwd_fp8(rq["q8"], rq["k8"], rq["vt8"], rq["q_scale"], rq["k_scale"], rq["v_scale"],
+                                 T, H, W, ph, pw, out["kv_idx"], out["kv_cnt"])
+    torch.cuda.synchronize()
+    opn = to_host(op)
+    g = oracle.draft_grid(T, H, W, ph, pw)
+    perm, _, _ = oracle.draft_permutation(g)
+    assert np.all(opn[:, perm < 0] == 0)  # pad rows of the reordered output
+    return o, o2, out
+
+
+DRAFT_FP8 = [
+    # T, H, W, pool_h, pool_w, heads, sparsity
+    (3, 45, 80, 8, 16, 2, 0.9),   # HunyuanVideo frames: 5-row edge tiles
+    (2, 20, 32, 8, 16, 2, 0.5),   # ragged tile rows
+    (2, 16, 32, 8, 8, 2, 0.5),    # 8-wide pools: raster tiles through 4-byte V pieces
+    (1, 8, 48, 4, 16, 3, 0.0),    # 64-token blocks, k = nb
+]
+
+
+@pytest.mark.parametrize("T,H,W,ph,pw,heads,sp", DRAFT_FP8)
+def test_fp8_draft_k_zero_is_mean_of_v(T, H, W, ph, pw, heads, sp):
+    """K = 0, integer-valued V: every probability is exactly 1, so each token's
+    output is the mean of V over its Draft key set (the mask comes from the
+    real Q and K, so the lists are the article's)."""
+    torch = _torch()
+    q, k, _ = synth.video_qkv(41, heads, T, H, W, 128)
+    n = T * H * W
+    vi = synth.bf16_round(_integer_v(np.random.default_rng(n), heads, n, 128))  # exact in bf16
+    note(f"fp8 draft K=0 T={T} H={H} W={W} pool={ph}x{pw} sp={sp}")
+    # the mask from the real Q, K; attention on K = 0
+    dq, dk = to_dev(q), to_dev(k)
+    out = _lib.draft_mask_and_perm(dq, dk, to_dev(vi), T, H, W, ph, pw, sp)
+    kz = torch.zeros_like(dk)
+    rq = _lib.quantize_qkv_fp8(dq, kz, to_dev(vi))
+    o2 = to_host(_lib.draft_attn_fwd_fp8(rq["q8"], rq["k8"], rq["vt8"], rq["q_scale"], rq["k_scale"],
+                                         rq["v_scale"], T, H, W, ph, pw, out["kv_idx"], out["kv_cnt"]))
+    bs = ph * pw
+    kzp = torch.zeros_like(out["k_perm"])
+    pq = _lib.quantize_qkv_fp8(out["q_perm"], kzp, out["v_perm"])
+    op = _lib.block_sparse_attn_fwd_fp8(pq["q8"], pq["k8"], pq["vt8"], pq["q_scale"], pq["k_scale"], pq["v_scale"],
+                                        bs, bs, out["kv_idx"], out["kv_cnt"], mask_heads=heads,
+                                        block_valid=out["block_valid"])
+    o = to_host(_lib.token_permute(op, out["inv_perm"]))
+    g = oracle.draft_grid(T, H, W, ph, pw)
+    perm, inv, bv = oracle.draft_permutation(g)
+    ref = oracle.draft_attention_original_order(np.zeros((heads, n, 128)), np.zeros((heads, n, 128)),
+                                                synth.bf16_to_f32(vi), perm, inv, bv, g.block_size,
+                                                to_host(out["kv_idx"]), to_host(out["kv_cnt"]))
+    _assert_exact_mean(o, ref, "draft reorder K=0")
+    _assert_exact_mean(o2, ref, "draft raster K=0")
+
+
+@pytest.mark.parametrize("T,H,W,ph,pw,heads,sp", DRAFT_FP8)
+def test_fp8_draft_within_bound_and_paths_agree(T, H, W, ph, pw, heads, sp):
+    """Random video-shaped inputs: the reorder and raster paths agree bit for
+    bit (full-width tiles: same keys, same tiles, same order), and match the
+    oracle on the dequantized values within the derived bound."""
+    torch = _torch()
+    q, k, v = synth.video_qkv(43, heads, T, H, W, 128)
+    note(f"fp8 draft T={T} H={H} W={W} pool={ph}x{pw} sp={sp}")
+    o, o2, out = _draft_fp8_both(q, k, v, T, H, W, ph, pw, sp)
+    assert torch.equal(o, o2)
+    deq = [oracle.dequantize(*oracle.quantize_per_head(synth.bf16_to_f32(x))) for x in (q, k, v)]
+    g = oracle.draft_grid(T, H, W, ph, pw)
+    perm, inv, bv = oracle.draft_permutation(g)
+    kv, cnt = to_host(out["kv_idx"]), to_host(out["kv_cnt"])
+    ref, bound, model, slack = (oracle.draft_attention_original_order(*deq, perm, inv, bv, g.block_size, kv, cnt, fn=f)
+                                for f in (None, oracle.p_rounding_bound, oracle.attention_p_e4m3, _acc_slack))
+    _assert_within_bound(to_host(o), ref, bound, model, float(np.abs(deq[2]).max()), f"draft fp8 sp={sp}", slack)
+
+
+def test_full_hunyuan_draft_fp8():
+    """HunyuanVideo Draft at full size (33 frames of 45x80, 24 heads, pool 8x16,
+    90 %): both FP8 paths bit-equal; sampled rows of three heads within the
+    derived bound of the oracle on the dequantized values."""
+    torch = _torch()
+    w = synth.WORKLOADS["hunyuan-draft"]
+    q, k, v = synth.video_qkv(w.seed, w.heads, w.T, w.H, w.W, w.d)
+    note("hunyuan draft fp8 both paths, full size")
+    o, o2, out = _draft_fp8_both(q, k, v, w.T, w.H, w.W, w.pool_h, w.pool_w, w.sparsity)
+    assert torch.equal(o, o2)
+    heads = [0, 9, 23]
+    deq = [oracle.dequantize(*oracle.quantize_per_head(synth.bf16_to_f32(x[heads]))) for x in (q, k, v)]
+    g = oracle.draft_grid(w.T, w.H, w.W, w.pool_h, w.pool_w)
+    perm, inv, bv = oracle.draft_permutation(g)
+    kv, cnt = to_host(out["kv_idx"])[heads], to_host(out["kv_cnt"])[heads]
+    rows = sample_frame_rows(np.random.default_rng(800), w.T, w.P, nframes=4, per_frame=48)
+    ref, bound, model, slack = (
+        oracle.draft_attention_original_order(*deq, perm, inv, bv, g.block_size, kv, cnt, rows=rows, fn=f)
+        for f in (None, oracle.p_rounding_bound, oracle.attention_p_e4m3, _acc_slack))
+    got = to_host(o)[heads][:, rows]
+    _assert_within_bound(got, ref, bound, model, float(np.abs(deq[2]).max()), "hunyuan draft fp8", slack)
+    del o, o2, out
+    torch.cuda.empty_cache()

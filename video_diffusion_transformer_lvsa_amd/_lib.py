@@ -37,7 +37,8 @@ SIGNATURES = {
     "draft_attn_fwd": (_c_int, [_p] * 4 + [_c_int] * 8 + [_p, _p, _c_int, _c_flt, _p]),
     "quantize_fp8_e4m3": (_c_int, [_p] + [_c_int] * 6 + [_p, _p, _p]),
     "block_sparse_attn_fwd_fp8": (_c_int, [_p] * 3 + [_c_int] + [_p] * 4 + [_c_int] * 5
-                                  + [_p, _p, _c_int, _c_int, _c_flt, _p]),
+                                  + [_p, _p, _c_int, _c_int, _p, _c_flt, _p]),
+    "draft_attn_fwd_fp8": (_c_int, [_p] * 3 + [_c_int] + [_p] * 4 + [_c_int] * 7 + [_p, _p, _c_int, _c_flt, _p]),
     "dense_attn_fwd_fp8": (_c_int, [_p] * 3 + [_c_int] + [_p] * 4 + [_c_int] * 3 + [_c_flt, _p]),
 }
 
@@ -298,18 +299,35 @@ def quantize_qkv_fp8(q, k, v, stream=None) -> dict:
 
 
 def block_sparse_attn_fwd_fp8(q8, k8, vt8, q_scale, k_scale, v_scale, block_q: int, block_k: int, kv_idx, kv_cnt,
-                              mask_heads: int = 1, scale: float | None = None, out=None, stream=None):
+                              mask_heads: int = 1, block_valid=None, scale: float | None = None, out=None,
+                              stream=None):
     """Block-sparse attention on E4M3 codes (vt8 [heads, 128, ldv]); returns O fp32 [heads, n, 128]."""
+    torch = _torch()
+    heads, n, d = q8.shape
+    if out is None:
+        out = torch.empty((heads, n, d), dtype=torch.float32, device=q8.device)
+    _contig_cuda(q8, k8, vt8, q_scale, k_scale, v_scale, out, kv_idx, kv_cnt, block_valid)
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    _check(load().block_sparse_attn_fwd_fp8(_ptr(q8), _ptr(k8), _ptr(vt8), vt8.shape[-1], _ptr(q_scale),
+                                            _ptr(k_scale), _ptr(v_scale), _ptr(out), heads, n, d, block_q, block_k,
+                                            _ptr(kv_idx), _ptr(kv_cnt), kv_idx.shape[-1], mask_heads,
+                                            _ptr(block_valid), scale, _stream(stream)))
+    return out
+
+
+def draft_attn_fwd_fp8(q8, k8, vt8, q_scale, k_scale, v_scale, T: int, H: int, grid_w: int, pool_h: int,
+                       pool_w: int, kv_idx, kv_cnt, scale: float | None = None, out=None, stream=None):
+    """FP8 Draft attention on the raster layout: codes of q, k [heads, T*H*grid_w, 128] and
+    vt8 [heads, 128, ldv], per-head lists kv_idx [heads, nb, k], kv_cnt [heads, nb]; returns O fp32."""
     torch = _torch()
     heads, n, d = q8.shape
     if out is None:
         out = torch.empty((heads, n, d), dtype=torch.float32, device=q8.device)
     _contig_cuda(q8, k8, vt8, q_scale, k_scale, v_scale, out, kv_idx, kv_cnt)
     scale = 1.0 / math.sqrt(d) if scale is None else scale
-    _check(load().block_sparse_attn_fwd_fp8(_ptr(q8), _ptr(k8), _ptr(vt8), vt8.shape[-1], _ptr(q_scale),
-                                            _ptr(k_scale), _ptr(v_scale), _ptr(out), heads, n, d, block_q, block_k,
-                                            _ptr(kv_idx), _ptr(kv_cnt), kv_idx.shape[-1], mask_heads, scale,
-                                            _stream(stream)))
+    _check(load().draft_attn_fwd_fp8(_ptr(q8), _ptr(k8), _ptr(vt8), vt8.shape[-1], _ptr(q_scale), _ptr(k_scale),
+                                     _ptr(v_scale), _ptr(out), heads, T, H, grid_w, d, pool_h, pool_w, _ptr(kv_idx),
+                                     _ptr(kv_cnt), kv_idx.shape[-1], scale, _stream(stream)))
     return out
 
 

@@ -486,7 +486,7 @@ int quantize_fp8_e4m3(const void* src, int dt, int heads, int n, int d, int tran
 int block_sparse_attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* vt8, int ldv,
                               const float* q_scale, const float* k_scale, const float* v_scale, float* o, int heads,
                               int n, int d, int block_q, int block_k, const int32_t* kv_idx, const int32_t* kv_cnt,
-                              int max_kv, int mask_heads, float scale, void* stream) {
+                              int max_kv, int mask_heads, const int32_t* block_valid, float scale, void* stream) {
   clear_err();
   int rc = check_fp8_attn(q8, k8, vt8, ldv, q_scale, k_scale, v_scale, o, heads, n, d, scale);
   if (rc) return rc;
@@ -495,6 +495,7 @@ int block_sparse_attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_
     return fail(LVSA_EUNSUPPORTED, "block_k=%d: the FP8 kernel needs block_k >= 64 and a multiple of 4", block_k);
   if (max_kv < 0) return fail(LVSA_EINVAL, "max_kv=%d must be >= 0", max_kv);
   if (mask_heads != 1 && mask_heads != heads) return fail(LVSA_EINVAL, "mask_heads=%d must be 1 or heads=%d", mask_heads, heads);
+  if (block_valid && block_q != block_k) return fail(LVSA_EINVAL, "block_valid requires block_q == block_k");
   if (heads == 0 || n == 0) return LVSA_OK;
   if (!kv_cnt || (max_kv > 0 && !kv_idx)) return fail(LVSA_EINVAL, "kv_cnt (and kv_idx when max_kv > 0) must be non-NULL");
   const long long nqb = ((long long)n + block_q - 1) / block_q;
@@ -502,6 +503,7 @@ int block_sparse_attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_
   if ((long long)nkb * block_k >= (1ll << 31) || (long long)max_kv * block_k >= (1ll << 31))
     return fail(LVSA_EINVAL, "key list spans more than 2^31 rows");
   lvsa::AttnArgs a{};
+  a.block_valid = block_valid;
   a.q = q8;
   a.k = k8;
   a.v = vt8;
@@ -546,6 +548,65 @@ int dense_attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* vt8,
   a.dense = 1;
   a.ldv = ldv;
   return run_fp8(a, q_scale, k_scale, v_scale, stream);
+}
+
+int draft_attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* vt8, int ldv, const float* q_scale,
+                       const float* k_scale, const float* v_scale, float* o, int heads, int T, int H, int grid_w,
+                       int d, int pool_h, int pool_w, const int32_t* kv_idx, const int32_t* kv_cnt, int max_kv,
+                       float scale, void* stream) {
+  clear_err();
+  lvsa::DraftGeom g;
+  int rc = geom(T, H, grid_w, pool_h, pool_w, &g);
+  if (rc) return rc;
+  if (grid_w % 4 != 0) return fail(LVSA_EUNSUPPORTED, "FP8 Draft attention needs grid_w a multiple of 4 (got %d)", grid_w);
+  rc = check_fp8_attn(q8, k8, vt8, ldv, q_scale, k_scale, v_scale, o, heads, g.n, d, scale);
+  if (rc) return rc;
+  if (g.bs % 64 != 0 || 64 % pool_w != 0 || pool_w < 4)
+    return fail(LVSA_EUNSUPPORTED,
+                "pool %dx%d: pool_h*pool_w must be a multiple of 64 and pool_w one of 4, 8, 16, 32, 64", pool_h,
+                pool_w);
+  if (max_kv < 0) return fail(LVSA_EINVAL, "max_kv=%d must be >= 0", max_kv);
+  if (heads == 0) return LVSA_OK;
+  if (!kv_cnt || (max_kv > 0 && !kv_idx)) return fail(LVSA_EINVAL, "kv_cnt (and kv_idx when max_kv > 0) must be non-NULL");
+  if ((long long)max_kv * g.bs >= (1ll << 31)) return fail(LVSA_EINVAL, "key list spans more than 2^31 rows");
+  lvsa::AttnArgs a{};
+  a.q = q8;
+  a.k = k8;
+  a.v = vt8;
+  a.o = o;
+  a.heads = heads;
+  a.n = g.n;
+  a.block_q = g.bs;
+  a.block_k = g.bs;
+  a.nqb = g.nb;
+  a.nkb = g.nb;
+  a.kv_idx = kv_idx;
+  a.kv_cnt = kv_cnt;
+  a.max_kv = max_kv;
+  a.mask_heads = heads;
+  a.scale = scale;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.ldv = ldv;
+  a.tile2d = 1;
+  a.gH = H;
+  a.gW = grid_w;
+  a.ph = pool_h;
+  a.pw = pool_w;
+  a.nbh = g.nbh;
+  a.nbw = g.nbw;
+  a.rpt = 64 / pool_w;
+  a.lpw = 0;
+  while ((1 << a.lpw) < pool_w) ++a.lpw;
+  a.inv_per = 1.0f / (float)(g.nbh * g.nbw);
+  a.inv_nbw = 1.0f / (float)g.nbw;
+  a.tiles_per_qb = (g.bs + lvsa::kBM_BF16 - 1) / lvsa::kBM_BF16;
+  const long long total = (long long)heads * g.nb * a.tiles_per_qb;
+  if (total >= (1ll << 31)) return fail(LVSA_EINVAL, "too many query tiles (%lld)", total);
+  a.total_tiles = (int)total;
+  rc = check_device();
+  if (rc) return rc;
+  return launched(lvsa::launch_draft_attn_fp8(a, q_scale, k_scale, v_scale, reinterpret_cast<hipStream_t>(stream)),
+                  "FP8 Draft attention launch");
 }
 
 }  // extern "C"

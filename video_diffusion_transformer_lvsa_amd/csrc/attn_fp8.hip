@@ -92,9 +92,27 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bsa_fwd_fp8_kernel(AttnArgs a
 
   const int blk_lo = qb * a.block_q;
   const int blk_end = min(blk_lo + a.block_q, a.n);
+  int qlim = a.block_q;
+  if (MODE == MODE_LIST && a.block_valid) {
+    const int bv = a.block_valid[qb];
+    qlim = bv < 0 ? 0 : (bv < qlim ? bv : qlim);
+  }
+  const int qend = min(blk_lo + qlim, blk_end);
   const int row_lo = blk_lo + qt * BM;
-  const int qrow = row_lo + wave * 32 + l32;
-  const bool q_valid = qrow < blk_end;
+  int qrow = row_lo + wave * 32 + l32;
+  bool q_in_blk = qrow < blk_end;  // output row to write (0 for pad rows)
+  bool q_valid = qrow < qend;      // query with keys
+  bool no_queries = row_lo >= qend;
+  if (MODE == MODE_T2D) {
+    // Query block qb is a raster pool tile; slot s = (s / pw, s % pw).
+    const BlkGeom gq = blk_geom(a, qb);
+    const int slot = qt * BM + wave * 32 + l32;
+    const int hi = slot >> a.lpw, wi = slot & (a.pw - 1);
+    q_valid = slot < a.block_q && hi < gq.vh && wi < gq.vw;
+    q_in_blk = q_valid;
+    qrow = q_valid ? gq.tok + hi * a.gW + wi : 0;
+    no_queries = ((qt * BM) >> a.lpw) >= gq.vh;
+  }
 
   const size_t head_off = (size_t)h * (size_t)a.n * D;  // bytes: one byte per element
   const int head_bytes = a.n * D;
@@ -117,7 +135,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bsa_fwd_fp8_kernel(AttnArgs a
     list = a.kv_idx + (size_t)base * a.max_kv;
     L = cnt * a.block_k;
   }
-  if (row_lo >= blk_end) L = 0;
+  if (no_queries) L = 0;
   const int ntiles = (L + BN - 1) / BN;
 
   // Qᵀ operand: lane (query l32, half) holds d = 64 s + 32 half .. +31.
@@ -139,16 +157,18 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bsa_fwd_fp8_kernel(AttnArgs a
   // key krow(R).
   constexpr int KJ = 8 / NW, VJ = 8 / NW, VJ4 = 32 / NW;
   const int kr_l = lane >> 3, kc_l = lane & 7;
+  // MODE_T2D (pw = 16): tile key k is token base0 + (k / 16) * W + k % 16.
+  auto key_off = [&](int k) { return MODE == MODE_T2D ? (k >> 4) * a.gW + (k & 15) : k; };
   unsigned kdma[KJ];
 #pragma unroll
   for (int j = 0; j < KJ; ++j) {
     const int R = 8 * (NW * j + wave) + kr_l;
-    kdma[j] = (unsigned)(krow(R) * 128 + 16 * (kc_l ^ ((R >> 1) & 7)));
+    kdma[j] = (unsigned)(key_off(krow(R)) * 128 + 16 * (kc_l ^ ((R >> 1) & 7)));
   }
   // Vᵀ loads (16 B): instruction j of wave `wave` fills the 1 KB chunk
   // c = NW*j + wave, rows d = 16c + lane/4, LDS chunk lane%4.
   const int vd_l = lane >> 2, vc_l = lane & 3;
-  const unsigned vdma = (unsigned)(vd_l * a.ldv + 16 * (vc_l ^ ((vd_l >> 2) & 3)));
+  const unsigned vdma = (unsigned)(vd_l * a.ldv + key_off(16 * (vc_l ^ ((vd_l >> 2) & 3))));
 
   unsigned kra[2][2];  // [k-step][16-byte half of the 32-byte operand] for key row l32 (+32 kb)
 #pragma unroll
@@ -166,10 +186,13 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bsa_fwd_fp8_kernel(AttnArgs a
   }
 
   // All BN rows valid and physically consecutive from base0: one run, or two
-  // runs of adjacent blocks (then base1 == base0). The 16-byte V pieces of
-  // such a tile start at any multiple of 4 bytes (base0 and a.ldv are), which
-  // the LDS-destination loads accept.
-  auto simple = [&](const TileD& t) { return t.full && (t.bnd >= BN || t.base1 == t.base0); };
+  // runs of adjacent blocks (then base1 == base0); MODE_T2D: a full tile of
+  // 16-wide pool rows (four runs of 16 tokens). The 16-byte V pieces of such
+  // a tile start at multiples of 4 bytes (base0, W and a.ldv are), which the
+  // LDS-destination loads accept.
+  auto simple = [&](const TileD& t) {
+    return MODE == MODE_T2D ? (t.full && a.pw == 16) : (t.full && (t.bnd >= BN || t.base1 == t.base0));
+  };
   auto dma16 = [&](__amdgpu_buffer_rsrc_t r, unsigned char* dst, unsigned voff, unsigned soff) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, voff, soff, 0, 0);
   };
@@ -210,7 +233,15 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bsa_fwd_fp8_kernel(AttnArgs a
         const int q = 4 * ((p4 >> 2) ^ ((d >> 2) & 3)) + (p4 & 3);
         const int p = tile_row<BN, MODE>(a, t, list, cnt, 4 * q);
         dma4(Vr, vb + 256 * (NW * j + wave), p >= 0 ? (unsigned)(d * a.ldv + p) : kInvalid);
-        if (j == 0 && wave == 0 && d == 0) kval[st][q] = p >= 0 ? 0x01010101u : 0u;
+        if (j == 0 && wave == 0 && d == 0) {
+          // One flag byte per key: the valid keys of a group are a prefix of
+          // it (runs and pool rows hold whole groups), and the group's other
+          // bytes of V are finite codes that meet probability 0.
+          unsigned f = 0u;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) f |= (tile_row<BN, MODE>(a, t, list, cnt, 4 * q + u) >= 0 ? 1u : 0u) << (8 * u);
+          kval[st][q] = f;
+        }
       }
     }
   };
@@ -339,8 +370,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bsa_fwd_fp8_kernel(AttnArgs a
   if (it < ntiles) step(0, s, sn);
 
   const float l_tot = half_sum(l_run);
-  const float inv = l_tot > 0.f ? vsc[h] / l_tot : 0.f;
-  if (q_valid) {
+  const float inv = l_tot > 0.f && q_valid ? vsc[h] / l_tot : 0.f;  // pad rows: 0
+  if (q_in_blk) {
     float* orow = Oh + (size_t)qrow * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
@@ -360,11 +391,19 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bsa_fwd_fp8_kernel(AttnArgs a
 // workgroup. So: eight waves when 256-row tiles leave no more idle rows in a
 // query block than 128-row tiles do.
 int fp8_waves(const AttnArgs& a) {
+  if (a.tile2d) return 4;
   const int r = a.block_q % 256;
   return (r == 0 || r > 128) ? 8 : 4;
 }
 
 }  // namespace
+
+hipError_t launch_draft_attn_fp8(const AttnArgs& a, const float* qs, const float* ks, const float* vs,
+                                 hipStream_t s) {
+  if (a.total_tiles == 0) return hipSuccess;
+  hipLaunchKernelGGL((bsa_fwd_fp8_kernel<MODE_T2D, 4>), dim3(a.total_tiles), dim3(256), 0, s, a, qs, ks, vs);
+  return hipGetLastError();
+}
 
 int fp8_rows_per_workgroup(const AttnArgs& a) { return 32 * fp8_waves(a); }
 

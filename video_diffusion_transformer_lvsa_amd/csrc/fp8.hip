@@ -7,8 +7,8 @@
 // fl32(x / scale) with the quotient clamped to [-448, 448], ties to even
 // (v_cvt_pk_fp8_f32 rounds to nearest even; it does not saturate, hence the
 // clamp). V may be written transposed, [heads, d, ld] (ld >= n, a multiple of
-// 16; bytes n .. ld-1 of a row are not written), which is the operand layout
-// the attention's PV product reads.
+// 16; bytes n .. ld-1 of a row are set to 0, so every byte of the operand is
+// a finite code), which is the operand layout the attention's PV product reads.
 #include "internal.h"
 
 namespace lvsa {
@@ -135,6 +135,13 @@ __global__ __launch_bounds__(256) void quant_t_kernel(const void* __restrict__ s
   }
   __syncthreads();
   const int full = min(64, n - t0);
+  if (blockIdx.x == gridDim.x - 1) {  // row padding n .. ld-1
+    const int padw = ld - n;
+    for (int c = threadIdx.x; c < d * padw; c += 256) {
+      const int ch = c / padw;
+      dst[((size_t)h * d + ch) * ld + n + (c - ch * padw)] = 0;
+    }
+  }
   for (int c = threadIdx.x; c < d * 4; c += 256) {  // 16-byte pieces of each channel row
     const int ch = c >> 2, p = (c & 3) * 16;
     uint8_t* out = dst + ((size_t)h * d + ch) * ld + t0 + p;

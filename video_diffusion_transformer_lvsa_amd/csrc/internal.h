@@ -55,6 +55,9 @@ hipError_t launch_attn_f32(const AttnArgs& a, int d, hipStream_t s);
 hipError_t launch_attn_fp8(const AttnArgs& a, const float* qs, const float* ks, const float* vs, hipStream_t s);
 // Query rows per workgroup of the FP8 kernel for these arguments.
 int fp8_rows_per_workgroup(const AttnArgs& a);
+// FP8 Draft attention on the raster layout (a.tile2d = 1).
+hipError_t launch_draft_attn_fp8(const AttnArgs& a, const float* qs, const float* ks, const float* vs,
+                                 hipStream_t s);
 
 hipError_t launch_lvsa_mask(int T, int C, int window, int T_per, int step, int32_t* kv_idx, int32_t* kv_cnt,
                             int cap, hipStream_t s);
