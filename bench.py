@@ -308,13 +308,35 @@ def run_draft(args, w):
     pool = args.pool
 
     reorder = not args.no_reorder
+    fp8 = bool(args.fp8)
     o_raster = None if reorder else torch.empty((w.heads, w.N, w.d), dtype=torch.float32, device=dev)
+    f8 = {}
 
     def mask():
         return _lib.draft_mask_and_perm(dq, dk, dv, w.T, w.H, w.W, w.pool_h, w.pool_w, sparsity, pool=pool,
                                         reorder=reorder)
 
+    def quantize(out):
+        # E4M3 codes of the tensors the attention reads (reordered or raster)
+        src = (out["q_perm"], out["k_perm"], out["v_perm"]) if reorder else (dq, dk, dv)
+        n = src[0].shape[1]
+        if not f8:
+            f8["q8"] = torch.empty((w.heads, n, w.d), dtype=torch.uint8, device=dev)
+            f8["k8"] = torch.empty_like(f8["q8"])
+            f8["vt8"] = torch.empty((w.heads, w.d, _lib.fp8_pitch(n)), dtype=torch.uint8, device=dev)
+            f8["sc"] = torch.empty((3, w.heads), dtype=torch.float32, device=dev)
+        _lib.quantize_fp8_e4m3(src[0], out=f8["q8"], scales=f8["sc"][0])
+        _lib.quantize_fp8_e4m3(src[1], out=f8["k8"], scales=f8["sc"][1])
+        _lib.quantize_fp8_e4m3(src[2], transpose=True, out=f8["vt8"], scales=f8["sc"][2])
+
     def attn(out):
+        if fp8:
+            c = (f8["q8"], f8["k8"], f8["vt8"], f8["sc"][0], f8["sc"][1], f8["sc"][2])
+            if reorder:
+                return _lib.block_sparse_attn_fwd_fp8(*c, bs, bs, out["kv_idx"], out["kv_cnt"], mask_heads=w.heads,
+                                                      block_valid=out["block_valid"])
+            return _lib.draft_attn_fwd_fp8(*c, w.T, w.H, w.W, w.pool_h, w.pool_w, out["kv_idx"], out["kv_cnt"],
+                                           out=o_raster)
         if reorder:
             return _lib.block_sparse_attn_fwd(out["q_perm"], out["k_perm"], out["v_perm"], bs, bs, out["kv_idx"],
                                               out["kv_cnt"], mask_heads=w.heads, block_valid=out["block_valid"])
@@ -323,6 +345,8 @@ def run_draft(args, w):
 
     def step():
         out = mask()
+        if fp8:
+            quantize(out)
         op = attn(out)
         o = _lib.token_permute(op, out["inv_perm"]) if reorder else op
         return out, op, o
@@ -335,6 +359,8 @@ def run_draft(args, w):
     pairs = int(sum((bv * bv[kv[h]].sum(axis=1)).sum() for h in range(w.heads)))
     e = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
     times = {"mask": [], "attn": [], "scatter": []}
+    if fp8:
+        times["quantize"] = []
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record(stream)
@@ -342,6 +368,9 @@ def run_draft(args, w):
         e[0].record(stream)
         out = mask()
         e[1].record(stream)
+        if fp8:
+            quantize(out)
+        e[4].record(stream)
         op = attn(out)
         e[2].record(stream)
         if reorder:
@@ -349,7 +378,9 @@ def run_draft(args, w):
         e[3].record(stream)
         torch.cuda.synchronize()
         times["mask"].append(e[0].elapsed_time(e[1]))
-        times["attn"].append(e[1].elapsed_time(e[2]))
+        if fp8:
+            times["quantize"].append(e[1].elapsed_time(e[4]))
+        times["attn"].append(e[4].elapsed_time(e[2]))
         times["scatter"].append(e[2].elapsed_time(e[3]))
     t1.record(stream)
     torch.cuda.synchronize()
@@ -367,18 +398,20 @@ def run_draft(args, w):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8-e4m3" if fp8 else "bf16",
         "data": "synthetic",
         "config": {"workload": f"hunyuanvideo-draft-{round(100 * sparsity)}pct" + ("-maxpool" if pool == "max" else "")
-                               + ("" if reorder else "-raster"),
+                               + ("" if reorder else "-raster") + ("-fp8" if fp8 else ""),
                    "T": w.T, "H": w.H, "W": w.W, "heads": w.heads, "d": w.d, "pool": [w.pool_h, w.pool_w],
                    "pooling": pool, "sparsity": sparsity, "top_k": int(kv.shape[-1]), "flop_per_call": flops},
         "stage_ms": {k2: round(sum(v2) / len(v2), 4) for k2, v2 in times.items()},
         "roofline": {"bound": "mfma", "achieved": round(flops / (attn_avg * 1e-3) / 1e12, 2),
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(flops / (attn_avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic_for(w.name, ATTN_SRC),
-                     "kernel": "bsa_fwd_d128_kernel<MODE_LIST, true>" if reorder else "bsa_fwd_d128_kernel<MODE_T2D, true>"},
+                     "peak": PEAK_FP8_TFLOPS if fp8 else PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(flops / (attn_avg * 1e-3) / 1e12 / (PEAK_FP8_TFLOPS if fp8 else PEAK_BF16_TFLOPS), 4),
+                     "traffic": None if fp8 else traffic_for(w.name, ATTN_SRC),
+                     "kernel": ("bsa_fwd_fp8_kernel<MODE_LIST, 4>" if reorder else "bsa_fwd_fp8_kernel<MODE_T2D, 4>")
+                     if fp8 else ("bsa_fwd_d128_kernel<MODE_LIST, true>" if reorder
+                                  else "bsa_fwd_d128_kernel<MODE_T2D, false>")},
     }
     return res
 
@@ -398,7 +431,8 @@ def main(argv=None) -> int:
                     help="Draft workload: attend on the raster layout (draft_attn_fwd) instead of reordering")
     ap.add_argument("--dense-steps", type=int, default=3)
     ap.add_argument("--fp8", action="store_true",
-                    help="LVSA workloads: quantize Q, K, V to E4M3 each step and run the FP8 attention")
+                    help="quantize Q, K, V (Draft: the tensors the attention reads) to E4M3 each step and run the "
+                         "FP8 attention")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="first run a plain row copy (token_permute, identity map) over this many MiB, 3 times, "
                          "so HBM counters can be scaled by a kernel of known traffic")
