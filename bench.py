@@ -408,7 +408,8 @@ def run_draft(args, w):
         "roofline": {"bound": "mfma", "achieved": round(flops / (attn_avg * 1e-3) / 1e12, 2),
                      "peak": PEAK_FP8_TFLOPS if fp8 else PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(flops / (attn_avg * 1e-3) / 1e12 / (PEAK_FP8_TFLOPS if fp8 else PEAK_BF16_TFLOPS), 4),
-                     "traffic": None if fp8 else traffic_for(w.name, ATTN_SRC),
+                     "traffic": (None if not reorder else
+                                 traffic_for(w.name + "-fp8", ATTN_FP8_SRC) if fp8 else traffic_for(w.name, ATTN_SRC)),
                      "kernel": ("bsa_fwd_fp8_kernel<MODE_LIST, 4>" if reorder else "bsa_fwd_fp8_kernel<MODE_T2D, 4>")
                      if fp8 else ("bsa_fwd_d128_kernel<MODE_LIST, true>" if reorder
                                   else "bsa_fwd_d128_kernel<MODE_T2D, false>")},

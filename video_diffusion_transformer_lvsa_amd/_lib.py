@@ -264,8 +264,9 @@ def draft_attn_fwd(q, k, v, T: int, H: int, grid_w: int, pool_h: int, pool_w: in
 # FP8 (E4M3) variant
 # --------------------------------------------------------------------------
 def fp8_pitch(n: int) -> int:
-    """Row pitch (bytes) of a transposed code tensor: n rounded up to 16."""
-    return (n + 15) // 16 * 16
+    """Row pitch (bytes) of a transposed code tensor: n rounded up to 128, so
+    every row starts on a cache line (the ABI needs only a multiple of 16)."""
+    return (n + 127) // 128 * 128
 
 
 def quantize_fp8_e4m3(x, transpose: bool = False, ld: int | None = None, out=None, scales=None, stream=None):
