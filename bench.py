@@ -42,6 +42,7 @@ WORKLOAD_NAMES = {
     "wan14b-6x": "wan2.1-14b-6x-lvsa",
     "hunyuan-draft": "hunyuanvideo-draft-90pct",
     "hunyuan-lvsa-2x": "hunyuanvideo-2x-lvsa",
+    "hunyuan-lvsa-1.5x": "hunyuanvideo-1.5x-lvsa",
 }
 
 

@@ -385,25 +385,26 @@ def test_full_wan14b_6x_lvsa_and_dense():
     torch.cuda.empty_cache()
 
 
-def test_full_hunyuan_lvsa_2x():
-    """LVSA on a HunyuanVideo-shaped grid at 2x training length: 65 latent
-    frames of 3600 tokens (the 128-row query tiles end in a 16-row tail),
-    budget 33 frames, 24 heads."""
+@pytest.mark.parametrize("name", ["hunyuan-lvsa-2x", "hunyuan-lvsa-1.5x"])
+def test_full_hunyuan_lvsa_long(name):
+    """LVSA on a HunyuanVideo-shaped grid at 2x and 1.5x training length: 65
+    and 49 latent frames of 3600 tokens (the 128-row query tiles end in a
+    16-row tail), budget 33 frames, 24 heads."""
     torch = _torch()
-    w, q, k, v = _full_inputs("hunyuan-lvsa-2x")
-    rng = np.random.default_rng(500)
+    w, q, k, v = _full_inputs(name)
+    rng = np.random.default_rng(500 + w.T)
     rows = sample_frame_rows(rng, w.T, w.P, nframes=4, per_frame=48)
     heads = [0, 11, 23]
     dq, dk, dv = to_dev(q), to_dev(k), to_dev(v)
     for s in (0, 5):
-        note(f"hunyuan-lvsa-2x s={s}")
+        note(f"{name} s={s}")
         idx, cnt = _lib.lvsa_mask(w.T, w.C, w.window, w.T_per, s)
         want_idx, want_cnt = oracle.lvsa_mask(w.T, w.C, w.window, w.T_per, s)
         assert np.array_equal(to_host(cnt), want_cnt)
         o = _lib.block_sparse_attn_fwd(dq, dk, dv, w.P, w.P, idx, cnt)
         got = to_host(o[heads])[:, rows]
         ref = oracle.block_sparse_attention(q, k, v, w.P, w.P, want_idx, want_cnt, rows=rows, heads=heads)
-        assert_attn_close(got, ref, what=f"hunyuan-lvsa-2x s={s}")
+        assert_attn_close(got, ref, what=f"{name} s={s}")
         del o
     del dq, dk, dv
     torch.cuda.empty_cache()

@@ -177,4 +177,6 @@ WORKLOADS = {
                           seed=5, C=21, window=5, T_per=8),
     "hunyuan-lvsa-2x": Workload("hunyuan-lvsa-2x", T=65, H=45, W=80, heads=24, d=128, dtype="bf16", kind="lvsa",
                                 seed=6, C=33, window=5, T_per=8),
+    "hunyuan-lvsa-1.5x": Workload("hunyuan-lvsa-1.5x", T=49, H=45, W=80, heads=24, d=128, dtype="bf16",
+                                  kind="lvsa", seed=7, C=33, window=5, T_per=8),
 }
