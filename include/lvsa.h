@@ -231,8 +231,9 @@ int dense_attn_fwd(const void* q, const void* k, const void* v, float* o, int dt
  * transpose = 1: dst [heads, d, ld], dst[h, c, i] = code of src[h, i, c];
  *   ld (row pitch in bytes) a multiple of 16 and >= n; bytes n .. ld-1 of a
  *   row are set to 0. This is the layout the attention takes V in.
- * scales: device float[heads], written. d is 64 or 128; n*d < 2^30 and
- * d*ld < 2^31. src, dst 16-byte aligned; scales 4-byte aligned. */
+ * scales: device float[heads], written. d is 64 or 128; n*d < 2^30,
+ * d*ld < 2^31, heads <= 65535. src, dst 16-byte aligned; scales 4-byte
+ * aligned. */
 int quantize_fp8_e4m3(const void* src, int dt, int heads, int n, int d, int transpose, int ld, uint8_t* dst,
                       float* scales, void* stream);
 

@@ -166,7 +166,8 @@ def test_fp8_validation(lib):
                          (0, None, _lib.LVSA_EINVAL),       # src
                          (7, MIS, _lib.LVSA_EINVAL),        # dst misaligned
                          (8, None, _lib.LVSA_EINVAL),       # scales
-                         (3, 1 << 23, _lib.LVSA_EINVAL)]:   # n*d >= 2^30
+                         (3, 1 << 23, _lib.LVSA_EINVAL),    # n*d >= 2^30
+                         (2, 65536, _lib.LVSA_EUNSUPPORTED)]:  # heads
         bad = list(ok)
         bad[i] = val
         assert qz(*bad) == code, (i, val)

@@ -464,6 +464,7 @@ int quantize_fp8_e4m3(const void* src, int dt, int heads, int n, int d, int tran
   if (dt != LVSA_F32 && dt != LVSA_BF16) return fail(LVSA_EINVAL, "dtype %d unknown", dt);
   if (d != 64 && d != 128) return fail(LVSA_EUNSUPPORTED, "head dim d=%d (supported: 64, 128)", d);
   if (heads < 0 || n < 0) return fail(LVSA_EINVAL, "heads=%d n=%d must be >= 0", heads, n);
+  if (heads > 65535) return fail(LVSA_EUNSUPPORTED, "heads=%d: at most 65535", heads);
   if ((long long)n * d >= (1ll << 30)) return fail(LVSA_EINVAL, "n*d=%lld exceeds 2^30", (long long)n * d);
   if (transpose != 0 && transpose != 1) return fail(LVSA_EINVAL, "transpose=%d must be 0 or 1", transpose);
   if (transpose) {
