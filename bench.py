@@ -22,6 +22,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -47,8 +48,14 @@ WORKLOAD_NAMES = {
 
 
 def src_hash(path: str) -> str:
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of a kernel source's code: comments and whitespace removed, so a
+    counter record stays valid across edits that change no code."""
+    with open(path) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    text = re.sub(r"\s+", "", text)
+    return hashlib.sha256(text.encode()).hexdigest()[:16]
 
 
 def log(msg: str):
@@ -68,7 +75,7 @@ def traffic_for(workload: str, kernel_src: str):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("kernel_src_sha256_16") != src_hash(kernel_src):
+    if t.get("kernel_code_sha256_16") != src_hash(kernel_src):
         return None
     return t.get("hbm_bytes_per_launch")
 

@@ -3,8 +3,9 @@
 //
 // What it computes ("LVSA: Training-Free Sparse Attention for Long Video
 // Diffusion", §1 problem statement and §2 complexity; the Draft Attention
-// article's block-sparse execution on reordered tokens): every query row
-// attends to the rows of the KV blocks listed for its query block,
+// article's block-sparse execution on reordered tokens, or in place on the
+// raster [t, h, w] layout where a block is a pool_h x pool_w tile): every
+// query row attends to the rows of the KV blocks listed for its query block,
 // O = softmax(scale * Q Kᵀ) V over those keys only.
 //
 // Design (one workgroup = 4 waves = 128 query rows; one wave = 32 rows):
@@ -37,6 +38,11 @@
 //    rescaled; probabilities stay <= 2^8, far inside bf16 and fp32 range.
 //  * Workgroup ids are remapped so that consecutive query tiles (same head,
 //    same query block, same key list) land on the same XCD and share its L2.
+//    Every workgroup of a block walks the same list with the same amount of
+//    work, so they stay in step and the L2 serves most K/V re-reads.
+//  * MODE_T2D (raster Draft): query and key blocks are pool tiles of the
+//    [t, h, w] grid; a 64-key tile is 64/pool_w pool rows, and a full tile of
+//    16-wide rows loads as four runs of 16 consecutive tokens.
 #include "attn_tiles.h"
 
 namespace lvsa {

@@ -4,21 +4,27 @@
 //
 // What it computes: the attention of "LVSA: Training-Free Sparse Attention
 // for Long Video Diffusion" (§1 problem statement, §2 complexity) over the
-// listed KV blocks, on per-head E4M3 codes of Q, K and V: with q = sq*Q8,
-// k = sk*K8, v = sv*V8 (codes decoded exactly), O = softmax(scale * q kᵀ) v.
-// The Draft Attention article names quantization as its next step.
+// listed KV blocks -- LVSA frame lists, or the Draft Attention article's
+// top-k blocks on the reordered tokens (with per-block valid counts) or on
+// the raster [t, h, w] layout -- on per-head E4M3 codes of Q, K and V: with
+// q = sq*Q8, k = sk*K8, v = sv*V8 (codes decoded exactly),
+// O = softmax(scale * q kᵀ) v. The Draft Attention article names
+// quantization as its next step.
 //
-// Design, as the bf16 kernel (one workgroup = 4 waves = 128 query rows, the
-// KV list walked as one virtual key sequence in 64-key tiles, one barrier per
-// tile, K two tiles and V one tile ahead, Sᵀ of tile i+1 on the matrix core
-// while tile i's softmax runs) with these differences:
+// Design, as the bf16 kernel (32 query rows per wave, the KV list walked as
+// one virtual key sequence in 64-key tiles, one barrier per tile, K two
+// tiles and V one tile ahead, Sᵀ of tile i+1 on the matrix core while tile
+// i's softmax runs) with these differences:
+//  * 4 or 8 waves per workgroup (128 or 256 query rows sharing each K/V
+//    tile), chosen per launch;
 //  * operands are bytes: a K tile is 64 rows x 128 B, a Vᵀ tile (V is given
 //    transposed, [heads, d, ldv]) is 128 rows x 64 B, each 8 KB; both come
 //    from global memory into LDS with LDS-destination buffer loads (16 B per
-//    lane; 4 B per lane where a Vᵀ row spans two runs that are not
-//    adjacent). Keys come in groups of 4 that are valid or not as a
-//    whole (n and block_k are multiples of 4), so one flag per group masks
-//    the scores of a partial tile;
+//    lane; 4 B per lane -- one group of 4 keys -- where a tile is not one
+//    physical run). Keys are valid as a prefix of each group of 4 (n and
+//    block_k are multiples of 4, pool rows hold whole groups), so a partial
+//    tile masks its scores with one flag byte per key, and the other bytes
+//    of a partly valid group are finite codes that meet probability 0;
 //  * the 32x32x64 MFMA operand layout (checked on the GPU): lane l holds row
 //    (A) or column (B) l mod 32 and k = 32*(l/32) .. +31, one byte each;
 //    Sᵀ = K Qᵀ takes 2 k-steps over d = 128, Oᵀ += Vᵀ Pᵀ one k-step over
