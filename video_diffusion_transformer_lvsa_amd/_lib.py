@@ -157,13 +157,15 @@ POOL_MODES = {"mean": 0, "max": 1}
 
 
 def draft_mask_and_perm(q, k, v, T: int, H: int, grid_w: int, pool_h: int, pool_w: int, sparsity: float,
-                        reorder: bool = True, pool: str = "mean", stream=None) -> dict:
+                        reorder: bool = True, pool: str = "mean", buffers: dict | None = None, stream=None) -> dict:
     """Draft mask builder + reorder. q, k, v: [heads, T*H*grid_w, d] on the GPU;
     pool is "mean" or "max".
 
     Returns a dict with kv_idx, kv_cnt, perm, inv_perm, block_valid, the
     reordered q_perm/k_perm/v_perm (if reorder) and qbar/kbar (views of the
-    workspace)."""
+    workspace). `buffers` may hold any of these outputs and "workspace"
+    (float32, draft_workspace_bytes / 4 elements), preallocated by the caller
+    (for instance for a captured graph); the others are allocated."""
     torch = _torch()
     heads, n, d = q.shape
     _contig_cuda(q, k, v)
@@ -171,19 +173,30 @@ def draft_mask_and_perm(q, k, v, T: int, H: int, grid_w: int, pool_h: int, pool_
     nb, n_pad, topk = info["nb"], info["n_pad"], info["k"]
     dev = q.device
     i32 = dict(dtype=torch.int32, device=dev)
+    given = buffers or {}
+
+    def buf(name, shape, **kw):
+        t = given.get(name)
+        if t is None:
+            return torch.empty(shape, **kw)
+        if tuple(t.shape) != tuple(shape) or t.dtype != kw["dtype"]:
+            raise ValueError(f"{name}: expected {kw['dtype']} {tuple(shape)}, got {t.dtype} {tuple(t.shape)}")
+        return t
+
     out = {
-        "kv_idx": torch.empty((heads, nb, topk), **i32),
-        "kv_cnt": torch.empty((heads, nb), **i32),
-        "perm": torch.empty((n_pad,), **i32),
-        "inv_perm": torch.empty((n,), **i32),
-        "block_valid": torch.empty((nb,), **i32),
+        "kv_idx": buf("kv_idx", (heads, nb, topk), **i32),
+        "kv_cnt": buf("kv_cnt", (heads, nb), **i32),
+        "perm": buf("perm", (n_pad,), **i32),
+        "inv_perm": buf("inv_perm", (n,), **i32),
+        "block_valid": buf("block_valid", (nb,), **i32),
         "info": info,
     }
     if reorder:
         for name in ("q_perm", "k_perm", "v_perm"):
-            out[name] = torch.empty((heads, n_pad, d), dtype=q.dtype, device=dev)
+            out[name] = buf(name, (heads, n_pad, d), dtype=q.dtype, device=dev)
     ws_bytes = draft_workspace_bytes(heads, T, H, grid_w, d, pool_h, pool_w)
-    ws = torch.empty((ws_bytes // 4,), dtype=torch.float32, device=dev)
+    ws = buf("workspace", (ws_bytes // 4,), dtype=torch.float32, device=dev)
+    _contig_cuda(*(t for key, t in out.items() if key != "info"), ws)
     _check(load().draft_mask_and_perm(
         _ptr(q), _ptr(k), _ptr(v), _dt(q), heads, T, H, grid_w, d, pool_h, pool_w, sparsity, POOL_MODES[pool],
         _ptr(out["kv_idx"]), _ptr(out["kv_cnt"]), _ptr(out["perm"]), _ptr(out["inv_perm"]), _ptr(out["block_valid"]),
