@@ -80,18 +80,42 @@ def traffic_for(workload: str, kernel_src: str):
     return t.get("hbm_bytes_per_launch")
 
 
+def oracle_threads() -> int:
+    """Threads the oracle's BLAS uses (else the affinity count)."""
+    try:
+        from threadpoolctl import threadpool_info
+
+        return max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # threadpoolctl missing: report the affinity count
+        return len(os.sched_getaffinity(0))
+
+
+def counters_for(workload: str, kernel_src: str):
+    """Counter evidence (clock, MFMA busy, L2 hit) from the committed rocprofv3
+    summary, if it was taken on the current kernel code; else None."""
+    path = os.path.join(ROOT, "profiles", f"counters_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_code_sha256_16") != src_hash(kernel_src):
+        return None
+    return t.get("metrics")
+
+
+def median(xs):
+    ys = sorted(xs)
+    m = len(ys) // 2
+    return ys[m] if len(ys) % 2 else 0.5 * (ys[m - 1] + ys[m])
+
+
 def cpu_baseline_lvsa(w, q, k, v, budget_s: float):
     """Time the fp64 oracle on whole query frames of the workload until ~budget_s."""
     import numpy as np
 
     import oracle
 
-    try:
-        from threadpoolctl import threadpool_info
-
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:  # threadpoolctl missing: report the affinity count
-        threads = len(os.sched_getaffinity(0))
+    threads = oracle_threads()
     idx, cnt = oracle.lvsa_mask(w.T, w.C, w.window, w.T_per, 0)
     rng = np.random.default_rng(0)
     frames = rng.permutation(w.T)
@@ -119,6 +143,49 @@ def cpu_baseline_lvsa(w, q, k, v, budget_s: float):
                   f"{dt:.1f} s",
         "seconds": dt,
         "ms_per_call_extrapolated": dt / pairs * (lvsa_pairs(w, cnt)) * 1e3,
+    }
+
+
+def cpu_baseline_draft(w, q, k, v, sparsity: float, pool: str, budget_s: float):
+    """Time the oracle on the Draft workload: the whole mask (pool, map, top-k)
+    for one head, then fp64 attention on whole query blocks of that head in
+    token order until ~budget_s."""
+    import numpy as np
+
+    import oracle
+    from video_diffusion_transformer_lvsa_amd import synth
+
+    threads = oracle_threads()
+    g = oracle.draft_grid(w.T, w.H, w.W, w.pool_h, w.pool_w)
+    perm, inv, bv = oracle.draft_permutation(g)
+    h = 0
+    t0 = time.perf_counter()
+    kv, cnt, *_ = oracle.draft_mask(synth.bf16_to_f32(q[h : h + 1]), synth.bf16_to_f32(k[h : h + 1]), g, sparsity,
+                                    pool=pool)
+    mask_s = time.perf_counter() - t0
+    rng = np.random.default_rng(0)
+    blocks = rng.permutation(g.nb)
+    pairs = 0
+    done = 0
+    t1 = time.perf_counter()
+    for b in blocks:
+        slots = perm[b * g.block_size : b * g.block_size + int(bv[b])]
+        oracle.draft_attention_original_order(q[h : h + 1], k[h : h + 1], v[h : h + 1], perm, inv, bv, g.block_size,
+                                              kv, cnt, rows=slots)
+        pairs += int(bv[b]) * int(sum(int(bv[x]) for x in kv[0, b, : cnt[0, b]]))
+        done += 1
+        if time.perf_counter() - t1 > budget_s:
+            break
+    dt = time.perf_counter() - t1
+    return {
+        "value": 4.0 * w.d * pairs / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"attention on {done} query blocks of head 0 (valid pairs, fp64 numpy, {dt:.1f} s); the mask "
+                  f"(pool, map, top-k) of one head timed separately",
+        "mask_seconds_per_head": round(mask_s, 3),
+        "seconds": dt + mask_s,
     }
 
 
@@ -255,6 +322,7 @@ def run_lvsa(args, w):
             "flop_per_call": flop_per_launch,
         },
         "attn_ms_per_call": round(attn_avg, 4),
+        "attn_ms_median": round(median(attn_ms), 4),
         "attn_ms_min": round(min(attn_ms), 4),
         "mask_build_ms": round(max(mask_ms, 0.0), 4),
         "pct_bf16_peak": round(100.0 * achieved / PEAK_BF16_TFLOPS, 2),
@@ -271,6 +339,9 @@ def run_lvsa(args, w):
         "traffic": traffic_for(w.name + ("-fp8" if fp8 else ""), ATTN_FP8_SRC if fp8 else ATTN_SRC),
         "kernel": "bsa_fwd_fp8_kernel<MODE_LIST, 4>" if fp8 else "bsa_fwd_d128_kernel<MODE_LIST, false>",
     }
+    ctr = counters_for(w.name + ("-fp8" if fp8 else ""), ATTN_FP8_SRC if fp8 else ATTN_SRC)
+    if ctr is not None:
+        res["counters"] = ctr
 
     if not args.no_dense:
         log("timing dense attention at the same shape")
@@ -289,6 +360,7 @@ def run_lvsa(args, w):
         res["dense_ms_per_call"] = round(dense_ms, 3)
         res["dense_tflops"] = round(dense_flops / (dense_ms * 1e-3) / 1e12, 2)
         res["speedup_vs_dense"] = round(dense_ms / attn_avg, 3)
+        res["dense_dtype"] = "fp8-e4m3" if fp8 else "bf16"
 
     if not args.no_cpu_baseline:
         log(f"timing the CPU oracle for ~{args.cpu_seconds} s")
@@ -365,6 +437,8 @@ def run_draft(args, w):
     kv = out["kv_idx"].cpu().numpy()
     bv = out["block_valid"].cpu().numpy().astype(np.int64)
     pairs = int(sum((bv * bv[kv[h]].sum(axis=1)).sum() for h in range(w.heads)))
+    cnt_all = out["kv_cnt"].cpu().numpy().astype(np.int64)
+    flops_area = 4.0 * w.d * bs * bs * float(cnt_all.sum())
     e = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
     times = {"mask": [], "attn": [], "scatter": []}
     if fp8:
@@ -394,6 +468,7 @@ def run_draft(args, w):
     torch.cuda.synchronize()
     ms_total = t0.elapsed_time(t1)
     attn_avg = sum(times["attn"]) / len(times["attn"])
+    attn_med = median(times["attn"])
     flops = 4.0 * w.d * pairs
     res = {
         "metric": METRIC,
@@ -411,8 +486,10 @@ def run_draft(args, w):
         "config": {"workload": f"hunyuanvideo-draft-{round(100 * sparsity)}pct" + ("-maxpool" if pool == "max" else "")
                                + ("" if reorder else "-raster") + ("-fp8" if fp8 else ""),
                    "T": w.T, "H": w.H, "W": w.W, "heads": w.heads, "d": w.d, "pool": [w.pool_h, w.pool_w],
-                   "pooling": pool, "sparsity": sparsity, "top_k": int(kv.shape[-1]), "flop_per_call": flops},
+                   "pooling": pool, "sparsity": sparsity, "top_k": int(kv.shape[-1]), "flop_per_call": flops,
+                   "flop_block_area_per_call": flops_area},
         "stage_ms": {k2: round(sum(v2) / len(v2), 4) for k2, v2 in times.items()},
+        "attn_ms_median": round(attn_med, 4),
         "roofline": {"bound": "mfma", "achieved": round(flops / (attn_avg * 1e-3) / 1e12, 2),
                      "peak": PEAK_FP8_TFLOPS if fp8 else PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(flops / (attn_avg * 1e-3) / 1e12 / (PEAK_FP8_TFLOPS if fp8 else PEAK_BF16_TFLOPS), 4),
@@ -422,6 +499,40 @@ def run_draft(args, w):
                      if fp8 else ("bsa_fwd_d128_kernel<MODE_LIST, true>" if reorder
                                   else "bsa_fwd_d128_kernel<MODE_T2D, false>")},
     }
+    if not args.no_dense:
+        # dense attention over the unpadded tokens at the same shape
+        # dense attention over the unpadded raster tokens at the same shape
+        # and arithmetic (FP8 codes of the raster tensors for an FP8 line)
+        log("timing dense attention at the same shape")
+        od = torch.empty((w.heads, w.N, w.d), dtype=torch.float32, device=dev)
+        if fp8:
+            c8 = _lib.quantize_qkv_fp8(dq, dk, dv)
+
+            def dense():
+                _lib.dense_attn_fwd_fp8(c8["q8"], c8["k8"], c8["vt8"], c8["q_scale"], c8["k_scale"], c8["v_scale"],
+                                        out=od)
+        else:
+            def dense():
+                _lib.dense_attn_fwd(dq, dk, dv, out=od)
+        dense()
+        torch.cuda.synchronize()
+        d0 = torch.cuda.Event(enable_timing=True)
+        d1 = torch.cuda.Event(enable_timing=True)
+        d0.record(stream)
+        for _ in range(args.dense_steps):
+            dense()
+        d1.record(stream)
+        torch.cuda.synchronize()
+        dense_ms = d0.elapsed_time(d1) / args.dense_steps
+        res["dense_ms_per_call"] = round(dense_ms, 3)
+        res["dense_tflops"] = round(4.0 * w.d * w.heads * float(w.N) * w.N / (dense_ms * 1e-3) / 1e12, 2)
+        res["speedup_vs_dense"] = round(dense_ms / attn_avg, 3)
+        res["speedup_vs_dense_pipeline"] = round(dense_ms / (ms_total / args.steps), 3)
+        res["dense_dtype"] = "fp8-e4m3" if fp8 else "bf16"
+        del od
+    if not args.no_cpu_baseline:
+        log(f"timing the CPU oracle for ~{args.cpu_seconds} s")
+        res["cpu_baseline"] = cpu_baseline_draft(w, q, k, v, sparsity, pool, args.cpu_seconds)
     return res
 
 

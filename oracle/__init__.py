@@ -41,6 +41,7 @@ from .draft import (
 from .fp8 import E4M3_MAX, e4m3_decode_table, e4m3_encode, quantize_per_head, dequantize, attention_p_e4m3, p_rounding_bound
 from .attention import (
     attention_keyset,
+    attention_statistics,
     dense_attention,
     block_sparse_attention,
     draft_attention_original_order,
@@ -55,6 +56,7 @@ __all__ = [
     "dequantize",
     "attention_p_e4m3",
     "p_rounding_bound",
+    "attention_statistics",
     "anchors",
     "nearest_order",
     "attend_set",

@@ -147,3 +147,29 @@ def draft_attention_original_order(q, k, v, perm, inv_perm, block_valid, block_s
             )
             out[hi, sel] = fn(to_f64(q[h, rows[sel]]), to_f64(k[h, keys]), to_f64(v[h, keys]), scale)
     return out
+
+
+def attention_statistics(q_rows: np.ndarray, k_all: np.ndarray, keep: np.ndarray, scale: float) -> dict:
+    """Statistics of the attention of q_rows [m, d] over all keys k_all [n, d],
+    and over the subset the mask keeps (boolean keep [m, n]).
+
+    Per row: the standard deviation of the scaled logits over all keys, the
+    entropy (nats) of the dense softmax, the entropy of the softmax restricted
+    to the kept keys, and the share of the dense softmax mass that falls on
+    the kept keys. Returns each as an array of m values."""
+    q_rows = np.asarray(q_rows, dtype=np.float64)
+    s = (q_rows @ np.asarray(k_all, dtype=np.float64).T) * scale
+    std = s.std(axis=1)
+
+    def entropy(logits, live):
+        z = np.where(live, logits, -np.inf)
+        m = z.max(axis=1, keepdims=True)
+        p = np.where(live, np.exp(z - m), 0.0)
+        p = p / p.sum(axis=1, keepdims=True)
+        return -(p * np.log(np.where(p > 0, p, 1.0))).sum(axis=1), p
+
+    everything = np.ones_like(keep, dtype=bool)
+    h_dense, p_dense = entropy(s, everything)
+    h_kept, _ = entropy(s, keep)
+    mass = (p_dense * keep).sum(axis=1)
+    return {"logit_std": std, "entropy_dense": h_dense, "entropy_kept": h_kept, "mass_kept": mass}
