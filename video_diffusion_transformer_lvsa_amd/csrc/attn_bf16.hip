@@ -30,12 +30,17 @@
 //  * Software pipeline, one barrier per tile: while the softmax of tile i
 //    runs on the VALU, the MFMAs of Sᵀ for tile i+1 run on the matrix core
 //    (K runs one tile ahead of V in LDS, two tiles ahead in global loads).
-//  * Probabilities are exp2(s*c - m*c), c = scale*log2(e), rounded to bf16
+//  * Probabilities are exp2(s*c - m), c = scale*log2(e), rounded to bf16
 //    for the PV product; the row sum accumulates the same rounded values
 //    (v_dot2_f32_bf16 against ones), so O is a convex combination of V rows
-//    up to fp32 accumulation. The reference max m is only moved when the
-//    tile max exceeds it by more than 8 (in log2 units), so O is rarely
-//    rescaled; probabilities stay <= 2^8, far inside bf16 and fp32 range.
+//    up to fp32 accumulation. The reference m is one of the row's scores
+//    (times c) and lags the running max: d = 128 computes a tile's
+//    probabilities against it without any row max, and only when a lane's
+//    probabilities of the tile sum to more than 2^16 (so one of them may be
+//    large) does the wave take the row max, move m to it, rescale O and
+//    recompute the tile. Probabilities stay <= 2^16, far inside bf16 and
+//    fp32 range. d = 64 moves m when the tile max exceeds it by more than
+//    8 (in log2 units).
 //  * Workgroup ids are remapped so that consecutive query tiles (same head,
 //    same query block, same key list) land on the same XCD and share its L2.
 //    Every workgroup of a block walks the same list with the same amount of
@@ -562,6 +567,29 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_d128_kernel(AttnArgs a) {
   const float c = a.scale_log2;
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
+  // exp2(s*c - m) of a tile's scores, rounded to bf16 into the B operand of
+  // the PV product; returns the lane's sum of the rounded values.
+  auto probs = [&](const f32x16 (&cur)[NKB], float m, bf16x8 (&pb)[PVSTEPS]) {
+    const float nm = (m == -INFINITY) ? 0.f : -m;
+    float t0 = 0.f, t1 = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < PVSTEPS; ++kk) {
+#pragma unroll
+      for (int j = 0; j < 8; j += 2) {
+        const float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(cur[kk >> 1][8 * (kk & 1) + j], c, nm));
+        const float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(cur[kk >> 1][8 * (kk & 1) + j + 1], c, nm));
+        const bf16x2 p2 = {(__bf16)x0, (__bf16)x1};
+        if (kk & 1)
+          t1 = __builtin_amdgcn_fdot2_f32_bf16(p2, ones, t1, false);
+        else
+          t0 = __builtin_amdgcn_fdot2_f32_bf16(p2, ones, t0, false);
+        pb[kk][j] = p2[0];
+        pb[kk][j + 1] = p2[1];
+      }
+    }
+    return t0 + t1;
+  };
+
   f32x16 s[NKB], sn[NKB];
   int full_cur = 1;
   TileStream ks;
@@ -608,39 +636,40 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_d128_kernel(AttnArgs a) {
 
       qk(st ^ 1, nxt);
 
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, cur[kb][r]);
-      mx = half_max(mx) * c;
-      const bool need = mx > mc + kRescale;
-      const float mc_new = need ? mx : mc;
-      const float alpha = need ? __builtin_amdgcn_exp2f(mc - mc_new) : 1.f;
-      mc = mc_new;
-      l_run *= alpha;
-      const float nm = (mc == -INFINITY) ? 0.f : -mc;
-
+      // Probabilities against the running reference mc, with no row max:
+      // a lane whose probabilities of this tile sum to more than kSumBf16
+      // (or whose row has no reference yet) sends the wave through the
+      // exact path, which moves mc to the row max, rescales and recomputes.
       bf16x8 pb[PVSTEPS];
+      float tl = probs(cur, mc, pb);
+      // Interleave the 16 Sᵀ MFMAs with their K reads (kept three ahead) and
+      // the softmax VALU work, which does not depend on them: a wave overlaps
+      // its own VALU work with its MFMAs only where the two are interleaved.
+      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
 #pragma unroll
-      for (int kk = 0; kk < PVSTEPS; ++kk) {
-#pragma unroll
-        for (int j = 0; j < 8; j += 2) {
-          const float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(cur[kk >> 1][8 * (kk & 1) + j], c, nm));
-          const float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(cur[kk >> 1][8 * (kk & 1) + j + 1], c, nm));
-          const bf16x2 p2 = {(__bf16)x0, (__bf16)x1};
-          l_run = __builtin_amdgcn_fdot2_f32_bf16(p2, ones, l_run, false);
-          pb[kk][j] = p2[0];
-          pb[kk][j + 1] = p2[1];
-        }
+      for (int i = 0; i < 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i < 13) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
       }
-
-      if (__ballot(need && (l_run == l_run)) != 0ull) {
+      if (__ballot(!(tl <= kSumBf16) || mc == -INFINITY) != 0ull) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, cur[kb][r]);
+        mx = half_max(mx) * c;
+        const float mc_new = fmaxf(mc, mx);
+        const float alpha = mc_new == mc ? 1.f : __builtin_amdgcn_exp2f(mc - mc_new);
+        mc = mc_new;
+        l_run *= alpha;
 #pragma unroll
         for (int i = 0; i < NDB; ++i)
 #pragma unroll
           for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
+        tl = probs(cur, mc, pb);
       }
+      l_run += tl;
 
 #pragma unroll
       for (int kk = 0; kk < PVSTEPS; ++kk) {
@@ -652,6 +681,13 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_d128_kernel(AttnArgs a) {
           const s16x4 both[2] = {lo, hi};
           oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, both), pb[kk], oacc[db], 0, 0, 0);
         }
+      }
+      // Vᵀ reads run eight (four MFMAs) ahead of the PV MFMAs.
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i < 12) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       }
 
     }

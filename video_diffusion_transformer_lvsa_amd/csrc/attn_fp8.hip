@@ -29,8 +29,12 @@
 //    (A) or column (B) l mod 32 and k = 32*(l/32) .. +31, one byte each;
 //    Sᵀ = K Qᵀ takes 2 k-steps over d = 128, Oᵀ += Vᵀ Pᵀ one k-step over
 //    the 64 keys of a tile;
-//  * probabilities are rounded to E4M3 (v_cvt_pk_fp8_f32, nearest even; they
-//    are <= 2^8 by the lazy reference max, inside the range). K rows sit in
+//  * probabilities are rounded to E4M3 (v_cvt_pk_fp8_f32, nearest even).
+//    They are computed against a lagging reference (one of the row's
+//    scores) with no row max; when a lane's probabilities of a tile sum to
+//    more than 2^8 the wave moves the reference to the row max, rescales
+//    and recomputes the tile, so every rounded probability is <= 2^8, inside
+//    the E4M3 range. K rows sit in
 //    LDS in a permuted order, row r = 32kb + 8g + 4h + i holding key
 //    32h + 16kb + 4g + i, so that the Sᵀ accumulator of lane (query, half h)
 //    holds exactly keys 32h .. 32h+31, in the byte order of the PV product's
@@ -275,6 +279,29 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bsa_fwd_fp8_kernel(AttnArgs a
   float l_run = 0.f;
   const float c = a.scale_log2 * qsc[h] * ksc[h];
 
+  // exp2(s*c - m) of a tile's scores in E4M3 as the Pᵀ operand: word
+  // 4kb + g holds the scores cur[kb][4g .. 4g+3], keys 32*half + 16kb + 4g +
+  // (0..3), so byte k of the operand is key 32*half + k. Returns the lane's
+  // sum of the unrounded values.
+  auto probs = [&](const f32x16 (&cur)[NKB], float m, i32x8& pB) {
+    const float nm = (m == -INFINITY) ? 0.f : -m;
+    float t0 = 0.f, t1 = 0.f;
+#pragma unroll
+    for (int kb2 = 0; kb2 < NKB; ++kb2)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        float p[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) p[t] = __builtin_amdgcn_exp2f(__builtin_fmaf(cur[kb2][4 * g + t], c, nm));
+        if (g & 1)
+          t1 += (p[0] + p[1]) + (p[2] + p[3]);
+        else
+          t0 += (p[0] + p[1]) + (p[2] + p[3]);
+        pB[4 * kb2 + g] = (int)pack4_fp8(p[0], p[1], p[2], p[3]);
+      }
+    return t0 + t1;
+  };
+
   f32x16 s[NKB], sn[NKB];
   int full_cur = 1;
   TileStream ks;
@@ -319,42 +346,31 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bsa_fwd_fp8_kernel(AttnArgs a
 
     qk(st ^ 1, nxt);
 
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb2 = 0; kb2 < NKB; ++kb2)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, cur[kb2][r]);
-    mx = half_max(mx) * c;
-    const bool need = mx > mc + kRescale;
-    const float mc_new = need ? mx : mc;
-    const float alpha = need ? __builtin_amdgcn_exp2f(mc - mc_new) : 1.f;
-    mc = mc_new;
-    l_run *= alpha;
-    const float nm = (mc == -INFINITY) ? 0.f : -mc;
-
-    // P in E4M3: word 4kb + g of the Pᵀ operand holds the scores
-    // cur[kb][4g .. 4g+3], keys 32*half + 16kb + 4g + (0..3): byte k of the
-    // operand is key 32*half + k.
+    // Probabilities against the running reference mc, with no row max: a
+    // lane whose probabilities of this tile sum to more than kSumFp8 (so one
+    // of them may exceed 2^8), or whose row has no reference yet, sends the
+    // wave through the exact path, which moves mc to the row max, rescales
+    // and recomputes.
     i32x8 pB;
+    float tl = probs(cur, mc, pB);
+    if (__ballot(!(tl <= kSumFp8) || mc == -INFINITY) != 0ull) {
+      float mx = -INFINITY;
 #pragma unroll
-    for (int kb2 = 0; kb2 < NKB; ++kb2)
+      for (int kb2 = 0; kb2 < NKB; ++kb2)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        float p[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          p[t] = __builtin_amdgcn_exp2f(__builtin_fmaf(cur[kb2][4 * g + t], c, nm));
-          l_run += p[t];
-        }
-        pB[4 * kb2 + g] = (int)pack4_fp8(p[0], p[1], p[2], p[3]);
-      }
-
-    if (__ballot(need && (l_run == l_run)) != 0ull) {
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, cur[kb2][r]);
+      mx = half_max(mx) * c;
+      const float mc_new = fmaxf(mc, mx);
+      const float alpha = mc_new == mc ? 1.f : __builtin_amdgcn_exp2f(mc - mc_new);
+      mc = mc_new;
+      l_run *= alpha;
 #pragma unroll
       for (int i = 0; i < NDB; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
+      tl = probs(cur, mc, pB);
     }
+    l_run += tl;
 
     const unsigned char* vb = vbuf(st);
 #pragma unroll

@@ -18,6 +18,8 @@ constexpr int kThreads = 256;
 constexpr int kBM = kBM_BF16;
 constexpr unsigned kInvalid = 0x80000000u;  // byte offset past every buffer: loads return 0
 constexpr float kRescale = 8.0f;            // log2 headroom before the reference max moves
+constexpr float kSumBf16 = 65536.0f;        // bf16 d = 128: largest lane sum of a tile's probabilities
+constexpr float kSumFp8 = 256.0f;           // FP8: the same, so that every probability is <= 2^8 < 448
 
 enum { MODE_DENSE = 0, MODE_LIST = 1, MODE_SMALL = 2, MODE_T2D = 3 };
 
