@@ -493,7 +493,9 @@ def run_draft(args, w):
         "roofline": {"bound": "mfma", "achieved": round(flops / (attn_avg * 1e-3) / 1e12, 2),
                      "peak": PEAK_FP8_TFLOPS if fp8 else PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(flops / (attn_avg * 1e-3) / 1e12 / (PEAK_FP8_TFLOPS if fp8 else PEAK_BF16_TFLOPS), 4),
-                     "traffic": (None if not reorder else
+                     # the counter records were taken on the reorder path at the workload's own
+                     # sparsity with mean pooling; other settings move other bytes
+                     "traffic": (None if not (reorder and sparsity == w.sparsity and pool == "mean") else
                                  traffic_for(w.name + "-fp8", ATTN_FP8_SRC) if fp8 else traffic_for(w.name, ATTN_SRC)),
                      "kernel": ("bsa_fwd_fp8_kernel<MODE_LIST, 4>" if reorder else "bsa_fwd_fp8_kernel<MODE_T2D, 4>")
                      if fp8 else ("bsa_fwd_d128_kernel<MODE_LIST, true>" if reorder
@@ -536,7 +538,172 @@ def run_draft(args, w):
     return res
 
 
+# ---------------------------------------------------------------------------
+# Summaries of rocprofv3 output (run on the host after the profiled runs):
+#   python3 bench.py --summarize traffic --workload W [--fp8] --fetch DIR --write DIR [--calib-copy-mb 1024]
+#   python3 bench.py --summarize counters --workload W [--fp8] --passes DIR DIR
+#   python3 bench.py --summarize trace --trace DIR --title T --cmd C --out FILE.md
+# traffic/counters write profiles/traffic_<key>.json / profiles/counters_<key>.json
+# with the code hash of the kernel source they were taken on.
+# ---------------------------------------------------------------------------
+def _csv_in(d: str, suffix: str):
+    import csv
+
+    for dirpath, _, files in os.walk(d):
+        for f in sorted(files):
+            if f.endswith(suffix):
+                with open(os.path.join(dirpath, f)) as fh:
+                    return list(csv.DictReader(fh))
+    raise FileNotFoundError(f"no *{suffix} under {d}")
+
+
+def _kernel_key(name: str) -> str:
+    for a in ("void ", "lvsa::(anonymous namespace)::", "lvsa::"):
+        name = name.replace(a, "")
+    return name.split("(")[0]
+
+
+def _per_kernel(rows, counter: str):
+    """{kernel: [value per dispatch]} for one counter."""
+    out = {}
+    for r in rows:
+        if r["Counter_Name"] == counter and "lvsa::" in r["Kernel_Name"]:
+            out.setdefault(_kernel_key(r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
+    return out
+
+
+def _profiled_kernel(workload: str, fp8: bool):
+    """(source, kernel key in traces, label, traffic/counter key, algorithmic bytes per launch)."""
+    from video_diffusion_transformer_lvsa_amd import synth
+
+    w = synth.WORKLOADS[workload]
+    if w.kind == "draft":
+        nb = w.T * (-(-w.H // w.pool_h)) * (-(-w.W // w.pool_w))
+        n = nb * w.pool_h * w.pool_w
+    else:
+        n = w.N
+    elem = 1 if fp8 else 2
+    alg = 3 * w.heads * n * w.d * elem + w.heads * n * w.d * 4
+    if fp8:
+        return ATTN_FP8_SRC, "bsa_fwd_fp8_kernel<1, 4>", "bsa_fwd_fp8_kernel<MODE_LIST, 4>", w.name + "-fp8", alg
+    tmpl = "bsa_fwd_d128_kernel<1, true>" if w.kind == "draft" else "bsa_fwd_d128_kernel<1, false>"
+    label = "bsa_fwd_d128_kernel<MODE_LIST, true>" if w.kind == "draft" else "bsa_fwd_d128_kernel<MODE_LIST, false>"
+    return ATTN_SRC, tmpl, label, w.name, alg
+
+
+def summarize(argv) -> int:
+    sp = argparse.ArgumentParser(prog="bench.py --summarize")
+    sp.add_argument("what", choices=("traffic", "counters", "trace"))
+    sp.add_argument("--workload", default="wan1.3b-6x")
+    sp.add_argument("--fp8", action="store_true")
+    sp.add_argument("--fetch")
+    sp.add_argument("--write")
+    sp.add_argument("--calib-copy-mb", type=int, default=1024)
+    sp.add_argument("--passes", nargs="+")
+    sp.add_argument("--trace")
+    sp.add_argument("--title")
+    sp.add_argument("--cmd", action="append", default=[])
+    sp.add_argument("--note", action="append", default=[])
+    sp.add_argument("--out")
+    a = sp.parse_args(argv)
+    if a.what == "trace":
+        rows = _csv_in(a.trace, "kernel_stats.csv")
+        lines = [f"# {a.title}", "", "Command (on one MI355X, from the repository root):", "", "```", *a.cmd, "```", "",
+                 "| kernel | calls | avg ms | min ms | max ms | % time |", "|---|---|---|---|---|---|"]
+        for r in rows[:10]:
+            lines.append(f"| `{_kernel_key(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e6:.4f} | "
+                         f"{float(r['MinNs']) / 1e6:.4f} | {float(r['MaxNs']) / 1e6:.4f} | "
+                         f"{float(r['Percentage']):.2f} |")
+        lines += ["", *a.note] if a.note else []
+        with open(a.out, "w") as f:
+            f.write("\n".join(lines) + "\n")
+        return 0
+    src, key, label, tkey, alg = _profiled_kernel(a.workload, a.fp8)
+    if a.what == "traffic":
+        fr, wr = _per_kernel(_csv_in(a.fetch, "counter_collection.csv"), "FETCH_SIZE"), \
+            _per_kernel(_csv_in(a.write, "counter_collection.csv"), "WRITE_SIZE")
+        rows = a.calib_copy_mb * (1 << 20) // 256
+        known_r, known_w = (rows * 256 + rows * 4) / 1024, rows * 256 / 1024
+        cal = "token_permute_kernel"
+        # the first three copy launches are the calibration (identity map over a known size)
+        cf = sum(fr[cal][:3]) / 3
+        cw = sum(wr[cal][:3]) / 3
+        ff, fw = known_r / cf, known_w / cw
+        mean = lambda v: sum(v) / len(v)
+        t = {"kernel": label, "workload": WORKLOAD_NAMES[a.workload] + ("-fp8" if a.fp8 else ""),
+             "kernel_code_sha256_16": src_hash(src),
+             "fetch_size_kib_raw": mean(fr[key]), "write_size_kib_raw": mean(wr[key]),
+             "copy_calibration": {"kernel": f"token_permute_kernel (identity map, {a.calib_copy_mb} MiB)",
+                                  "read_kib_known": known_r, "fetch_size_kib": cf, "write_kib_known": known_w,
+                                  "write_size_kib": cw, "fetch_factor": ff, "write_factor": fw},
+             "hbm_fetch_bytes_per_launch": mean(fr[key]) * ff * 1024,
+             "hbm_write_bytes_per_launch": mean(wr[key]) * fw * 1024,
+             "algorithmic_bytes_per_launch": alg,
+             "note": "FETCH_SIZE counts L2 misses, served by MALL or HBM",
+             "other_kernels_bytes_per_launch": {
+                 k: {"read": mean(fr[k] if k != cal else fr[k][3:] or fr[k]) * ff * 1024,
+                     "write": mean(wr[k] if k != cal else wr[k][3:] or wr[k]) * fw * 1024}
+                 for k in sorted(set(fr) & set(wr)) if k != key and (k != cal or len(fr[k]) > 3)},
+             "commands": a.cmd}
+        t["hbm_bytes_per_launch"] = t["hbm_fetch_bytes_per_launch"] + t["hbm_write_bytes_per_launch"]
+        out = a.out or os.path.join(ROOT, "profiles", f"traffic_{tkey}.json")
+    else:
+        got = {}
+        for d in a.passes:
+            rows = _csv_in(d, "counter_collection.csv")
+            for r in rows:
+                if _kernel_key(r["Kernel_Name"]) != key:
+                    continue
+                did = (d, r["Dispatch_Id"])
+                e = got.setdefault(r["Counter_Name"], {})
+                e[did] = float(r["Counter_Value"])
+                got.setdefault("_dur", {})[did] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+        m = {c: sum(v.values()) / len(v) for c, v in got.items()}
+        xcd, simds = 8, 1024
+        clk = m["GRBM_GUI_ACTIVE"] / xcd / m["_dur"]
+        cyc = m["GRBM_GUI_ACTIVE"] / xcd
+        mops = "SQ_INSTS_VALU_MFMA_MOPS_F8" if a.fp8 else "SQ_INSTS_VALU_MFMA_MOPS_BF16"
+        met = {"duration_ms_under_counters": round(m["_dur"] * 1e3, 2), "shader_clock_ghz": round(clk / 1e9, 3)}
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in m:
+            met["mfma_busy_frac"] = round(m["SQ_VALU_MFMA_BUSY_CYCLES"] / simds / cyc, 4)
+        if mops in m:
+            met["matrix_core_flop_per_launch"] = m[mops] * 512
+        if "SQ_INSTS_MFMA" in m:
+            met["mfma_insts_per_launch"] = m["SQ_INSTS_MFMA"]
+            if "SQ_INSTS_VALU" in m:
+                met["other_valu_per_mfma"] = round((m["SQ_INSTS_VALU"] - m["SQ_INSTS_MFMA"]) / m["SQ_INSTS_MFMA"], 3)
+        if "SQ_WAIT_INST_ANY" in m and "SQ_WAVE_CYCLES" in m:
+            met["dependency_wait_frac"] = round(m["SQ_WAIT_INST_ANY"] / m["SQ_WAVE_CYCLES"], 4)
+        if "SQ_VALU_MFMA_COEXEC_CYCLES" in m:
+            met["valu_mfma_coexec_frac"] = round(m["SQ_VALU_MFMA_COEXEC_CYCLES"] / simds / cyc, 4)
+        if "TCC_HIT_sum" in m and "TCC_MISS_sum" in m:
+            met["l2_hit_rate"] = round(m["TCC_HIT_sum"] / (m["TCC_HIT_sum"] + m["TCC_MISS_sum"]), 4)
+        if "SQ_LDS_BANK_CONFLICT" in m:
+            met["lds_bank_conflicts"] = m["SQ_LDS_BANK_CONFLICT"]
+        if "SQ_INSTS_LDS" in m:
+            met["lds_insts_per_launch"] = m["SQ_INSTS_LDS"]
+        t = {"kernel": label, "workload": WORKLOAD_NAMES[a.workload] + ("-fp8" if a.fp8 else ""),
+             "kernel_code_sha256_16": src_hash(src), "metrics": met,
+             "derivation": {"shader_clock_ghz": "GRBM_GUI_ACTIVE / 8 XCDs / dispatch duration",
+                            "mfma_busy_frac": "SQ_VALU_MFMA_BUSY_CYCLES / 1024 SIMDs / (GRBM_GUI_ACTIVE / 8)",
+                            "matrix_core_flop_per_launch": mops + " x 512",
+                            "other_valu_per_mfma": "(SQ_INSTS_VALU - SQ_INSTS_MFMA) / SQ_INSTS_MFMA",
+                            "dependency_wait_frac": "SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES",
+                            "valu_mfma_coexec_frac": "SQ_VALU_MFMA_COEXEC_CYCLES / 1024 / (GRBM_GUI_ACTIVE / 8)",
+                            "l2_hit_rate": "TCC_HIT_sum / (TCC_HIT_sum + TCC_MISS_sum)"},
+             "commands": a.cmd}
+        out = a.out or os.path.join(ROOT, "profiles", f"counters_{tkey}.json")
+    with open(out, "w") as f:
+        json.dump(t, f, indent=1)
+        f.write("\n")
+    print(f"wrote {out}")
+    return 0
+
+
 def main(argv=None) -> int:
+    argv = sys.argv[1:] if argv is None else argv
+    if argv and argv[0] == "--summarize":
+        return summarize(argv[1:])
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=16)
