@@ -12,9 +12,12 @@
 // quantization as its next step.
 //
 // Design, as the bf16 kernel (32 query rows per wave, the KV list walked as
-// one virtual key sequence in 64-key tiles, one barrier per tile, K two
-// tiles and V one tile ahead, Sᵀ of tile i+1 on the matrix core while tile
-// i's softmax runs) with these differences:
+// one virtual key sequence in 64-key tiles, one barrier per tile, Sᵀ of tile
+// i+1 on the matrix core while tile i's softmax runs) with these
+// differences:
+//  * a deeper pipeline: step i also runs the PV product of tile i-1 under
+//    the softmax of tile i (the softmax is the longer part here), so K is
+//    loaded two tiles ahead and V in the step before it is read;
 //  * 4 or 8 waves per workgroup (128 or 256 query rows sharing each K/V
 //    tile), chosen per launch;
 //  * operands are bytes: a K tile is 64 rows x 128 B, a Vᵀ tile (V is given
@@ -41,6 +44,8 @@
 //    B operand: the packed probabilities feed the matrix core as they are,
 //    with no exchange between the half-waves;
 //  * the row sum adds the unrounded fp32 probabilities.
+#include <type_traits>
+
 #include "attn_tiles.h"
 
 namespace lvsa {
@@ -81,7 +86,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bsa_fwd_fp8_kernel(AttnArgs a
   __shared__ __attribute__((aligned(1024))) unsigned char ks1[TILE];
   __shared__ __attribute__((aligned(1024))) unsigned char vs0[TILE];
   __shared__ __attribute__((aligned(1024))) unsigned char vs1[TILE];
-  __shared__ unsigned int kval[2][BN / 4];
+  __shared__ unsigned int kval[4][BN / 4];  // per-key flags of tile i in slot i % 4
   auto kbuf = [&](int st) -> unsigned char* { return st == 0 ? ks0 : ks1; };
   auto vbuf = [&](int st) -> unsigned char* { return st == 0 ? vs0 : vs1; };
 
@@ -209,7 +214,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bsa_fwd_fp8_kernel(AttnArgs a
   auto dma4 = [&](__amdgpu_buffer_rsrc_t r, unsigned char* dst, unsigned voff) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 4, voff, 0u, 0, 0);
   };
-  auto load_k = [&](const TileD& t, int st) {
+  // K of a tile, and (for a tile that is not full) one flag byte per key
+  // into kval[slot]: byte k is key k of the tile.
+  auto load_k = [&](const TileD& t, int st, int slot) {
     unsigned char* kb = kbuf(st);
     if (simple(t)) {
       const unsigned so = (unsigned)(t.base0 * D);
@@ -222,6 +229,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bsa_fwd_fp8_kernel(AttnArgs a
         const int p = tile_row<BN, MODE>(a, t, list, cnt, krow(R));
         const unsigned off = p >= 0 ? (unsigned)(p * 128 + 16 * (kc_l ^ ((R >> 1) & 7))) : kInvalid;
         dma16(Kr, kb + 1024 * (NW * j + wave), off, 0u);
+        // The valid keys of a group of 4 are a prefix of it (runs and pool
+        // rows hold whole groups); the other bytes of a partly valid group
+        // of V are finite codes that meet probability 0.
+        if (kc_l == 0) ((unsigned char*)kval[slot])[krow(R)] = p >= 0 ? 1 : 0;
       }
     }
   };
@@ -243,15 +254,6 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bsa_fwd_fp8_kernel(AttnArgs a
         const int q = 4 * ((p4 >> 2) ^ ((d >> 2) & 3)) + (p4 & 3);
         const int p = tile_row<BN, MODE>(a, t, list, cnt, 4 * q);
         dma4(Vr, vb + 256 * (NW * j + wave), p >= 0 ? (unsigned)(d * a.ldv + p) : kInvalid);
-        if (j == 0 && wave == 0 && d == 0) {
-          // One flag byte per key: the valid keys of a group are a prefix of
-          // it (runs and pool rows hold whole groups), and the group's other
-          // bytes of V are finite codes that meet probability 0.
-          unsigned f = 0u;
-#pragma unroll
-          for (int u = 0; u < 4; ++u) f |= (tile_row<BN, MODE>(a, t, list, cnt, 4 * q + u) >= 0 ? 1u : 0u) << (8 * u);
-          kval[st][q] = f;
-        }
       }
     }
   };
@@ -302,57 +304,83 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bsa_fwd_fp8_kernel(AttnArgs a
     return t0 + t1;
   };
 
+  // Oᵀ += Vᵀ Pᵀ over one tile (Vᵀ in stage st).
+  auto pv = [&](int st, const i32x8& pB) {
+    const unsigned char* vb = vbuf(st);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const i32x8 A = lds_read32(vb + db * 2048, vra[0], vra[1]);
+      oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, pB, oacc[db], 0, 0, 0, 0, 0, 0);
+    }
+  };
+
+  // Pipeline over tiles i = 0, 1, ...: step i loads K of tile i+2 and Vᵀ of
+  // tile i, runs Sᵀ of tile i+1 and PV of tile i-1 on the matrix core while
+  // the softmax of tile i runs on the VALU, then waits for its loads and
+  // meets the other waves at one barrier. K and Vᵀ of tile i sit in stage
+  // i % 2, so step i reads only stage (i+1) % 2 and fills only stage i % 2.
   f32x16 s[NKB], sn[NKB];
-  int full_cur = 1;
+  i32x8 pa, pz;
   TileStream ks;
   stream_init<BN, MODE>(ks, a, list, cnt, 0);
-  TileD tprev;
+  TileD tq0, tq1;  // descriptors of tiles i and i+1
   if (ntiles > 0) {
-    const TileD t0 = stream_tile<BN, MODE>(ks, a, L);
+    tq0 = stream_tile<BN, MODE>(ks, a, L);
     stream_next<BN, MODE>(ks, a, list, cnt);
-    const TileD t1 = stream_tile<BN, MODE>(ks, a, L);
+    tq1 = stream_tile<BN, MODE>(ks, a, L);
     stream_next<BN, MODE>(ks, a, list, cnt);
-    load_k(t0, 0);
-    load_v(t0, 0);
-    load_k(t1, 1);
-    full_cur = t0.full;
-    tprev = t1;
+    load_k(tq0, 0, 0);
+    load_k(tq1, 1, 1);
   }
   wait_dma();
   __syncthreads();
   if (ntiles > 0) qk(0, s);
   __syncthreads();
 
-  auto step = [&](const int st, f32x16 (&cur)[NKB], f32x16 (&nxt)[NKB]) {
+  auto step = [&](auto with_pv, const int st, const int i, f32x16 (&cur)[NKB], f32x16 (&nxt)[NKB],
+                  const i32x8& pprev, i32x8& pcur) {
     const TileD tk = stream_tile<BN, MODE>(ks, a, L);
     stream_next<BN, MODE>(ks, a, list, cnt);
-    const TileD tv = tprev;
-    tprev = tk;
-    load_k(tk, st);
-    load_v(tv, st ^ 1);
+    load_k(tk, st, (i + 2) & 3);
+    load_v(tq0, st);
+    const int full_i = tq0.full;
+    tq0 = tq1;
+    tq1 = tk;
 
-    if (!full_cur) {
+    if (!full_i) {
+      const unsigned* fl = kval[i & 3];
 #pragma unroll
       for (int kb2 = 0; kb2 < NKB; ++kb2)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          // score rows 32kb + 8g + 4h + i are keys 32h + 16kb + 4g + i
-          const unsigned f4 = kval[st][8 * half + 4 * kb2 + g];
+          // score rows 32kb + 8g + 4h + u are keys 32h + 16kb + 4g + u
+          const unsigned f4 = fl[8 * half + 4 * kb2 + g];
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (((f4 >> (8 * i)) & 0xffu) == 0u) cur[kb2][4 * g + i] = -INFINITY;
+          for (int u = 0; u < 4; ++u)
+            if (((f4 >> (8 * u)) & 0xffu) == 0u) cur[kb2][4 * g + u] = -INFINITY;
         }
     }
 
     qk(st ^ 1, nxt);
+    if constexpr (decltype(with_pv)::value) pv(st ^ 1, pprev);
 
     // Probabilities against the running reference mc, with no row max: a
     // lane whose probabilities of this tile sum to more than kSumFp8 (so one
     // of them may exceed 2^8), or whose row has no reference yet, sends the
     // wave through the exact path, which moves mc to the row max, rescales
     // and recomputes.
-    i32x8 pB;
-    float tl = probs(cur, mc, pB);
+    float tl = probs(cur, mc, pcur);
+    // Interleave the MFMAs (4 of Sᵀ, 4 of PV) with their LDS reads (kept
+    // ahead) and the softmax VALU work, which depends on neither.
+    if constexpr (decltype(with_pv)::value) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int g = 0; g < 8; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (g < 6) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);
+      }
+    }
     if (__ballot(!(tl <= kSumFp8) || mc == -INFINITY) != 0ull) {
       float mx = -INFINITY;
 #pragma unroll
@@ -364,32 +392,42 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bsa_fwd_fp8_kernel(AttnArgs a
       const float alpha = mc_new == mc ? 1.f : __builtin_amdgcn_exp2f(mc - mc_new);
       mc = mc_new;
       l_run *= alpha;
+      // O holds tiles up to i-1 against the old reference.
 #pragma unroll
-      for (int i = 0; i < NDB; ++i)
+      for (int u = 0; u < NDB; ++u)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
-      tl = probs(cur, mc, pB);
+        for (int r = 0; r < 16; ++r) oacc[u][r] *= alpha;
+      tl = probs(cur, mc, pcur);
     }
     l_run += tl;
 
-    const unsigned char* vb = vbuf(st);
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      const i32x8 A = lds_read32(vb + db * 2048, vra[0], vra[1]);
-      oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, pB, oacc[db], 0, 0, 0, 0, 0, 0);
-    }
-
-    full_cur = tv.full;
     wait_dma();
     __syncthreads();
   };
 
+  using no_pv = std::integral_constant<bool, false>;
+  using with_pv = std::integral_constant<bool, true>;
   int it = 0;
-  for (; it + 1 < ntiles; it += 2) {
-    step(0, s, sn);
-    step(1, sn, s);
+  if (ntiles > 0) {
+    step(no_pv{}, 0, 0, s, sn, pz, pa);
+    it = 1;
   }
-  if (it < ntiles) step(0, s, sn);
+  for (; it + 1 < ntiles; it += 2) {
+    step(with_pv{}, 1, it, sn, s, pa, pz);
+    step(with_pv{}, 0, it + 1, s, sn, pz, pa);
+  }
+  bool last_in_pz = false;
+  if (it < ntiles) {
+    step(with_pv{}, 1, it, sn, s, pa, pz);
+    last_in_pz = true;
+  }
+  // PV of the last tile (its Vᵀ in stage (ntiles-1) % 2).
+  if (ntiles > 0) {
+    if (last_in_pz)
+      pv(1, pz);
+    else
+      pv(0, pa);
+  }
 
   const float l_tot = half_sum(l_run);
   const float inv = l_tot > 0.f && q_valid ? vsc[h] / l_tot : 0.f;  // pad rows: 0
