@@ -64,3 +64,27 @@ def sample_frame_rows(rng, T: int, P: int, nframes: int = 6, per_frame: int = 96
         loc |= set(rng.choice(P, size=min(P, max(0, per_frame - len(loc))), replace=False).tolist())
         rows.extend(base + np.array(sorted(loc)))
     return np.array(rows, dtype=np.int64)
+
+
+# Per-tile offsets (one per 64-key tile) added to one channel of K, so that
+# scores jump by up to ~30 bits (base 2) from one tile of the key walk to the
+# next: the attention kernels then move their running reference, rescale O
+# and recompute the tile on many tiles, for some rows of a wave and not for
+# others (the rows weigh the channel differently).
+TILE_OFFSETS = {
+    "rising": lambda nt: 25.0 * np.arange(nt),
+    "zigzag": lambda nt: np.resize(np.array([0, 40, 10, 90, 95, 30, 160, 20, 161, 200, 5, 240], np.float64), nt),
+    "falling": lambda nt: 25.0 * (nt - 1 - np.arange(nt)),
+}
+
+
+def jumping_scores_qkv(seed: int, heads: int, ntile: int, d: int, pattern: str):
+    """fp32 Q, K, V [heads, 64*ntile, d]: N(0, 1) plus Q[:, :, 0] = 8 u (u
+    uniform in [0.05, 1] per row) and K[:, :, 0] += the offset of the key's
+    64-key tile."""
+    rng = np.random.default_rng(seed)
+    n = 64 * ntile
+    q, k, v = (rng.standard_normal((heads, n, d)).astype(np.float32) for _ in range(3))
+    q[:, :, 0] = 8.0 * rng.uniform(0.05, 1.0, size=(heads, n)).astype(np.float32)
+    k[:, :, 0] += np.repeat(TILE_OFFSETS[pattern](ntile), 64).astype(np.float32)[None, :]
+    return q, k, v

@@ -11,7 +11,7 @@ import pytest
 import oracle
 from video_diffusion_transformer_lvsa_amd import _lib, synth
 
-from helpers import assert_attn_close, note, sample_frame_rows, to_dev, to_host
+from helpers import TILE_OFFSETS, assert_attn_close, jumping_scores_qkv, note, sample_frame_rows, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -200,6 +200,32 @@ def test_bf16_closed_forms():
         live = o1[:, lo : lo + bv[b]]
         assert np.abs(live - vv[:, 200:201]).max() <= 1e-6
         assert np.all(o1[:, lo + bv[b] : lo + 100] == 0)  # pad query rows
+
+
+@pytest.mark.parametrize("pattern", sorted(TILE_OFFSETS))
+def test_bf16_running_reference_moves(pattern):
+    """Scores that jump between 64-key tiles: the exact path of the softmax
+    (reference moved to the row max, O and the row sum rescaled, tile
+    recomputed) runs on many tiles, wave-wide but for a subset of its rows.
+    Dense walks the keys in order; the block list walks the tiles in reverse
+    (rising becomes falling)."""
+    torch = _torch()
+    heads, ntile, d = 2, 12, 128
+    n = 64 * ntile
+    q, k, v = (synth.bf16_round(x) for x in jumping_scores_qkv(40 + len(pattern), heads, ntile, d, pattern))
+    dq, dk, dv = to_dev(q), to_dev(k), to_dev(v)
+    note(f"running reference, dense, {pattern}")
+    got = to_host(_lib.dense_attn_fwd(dq, dk, dv))
+    ref = oracle.dense_attention(q, k, v)
+    assert_attn_close(got, ref, what=f"dense {pattern}")
+    nqb = n // 128
+    idx = np.tile(np.arange(ntile, dtype=np.int32)[::-1], (1, nqb, 1))
+    cnt = np.full((1, nqb), ntile, dtype=np.int32)
+    note(f"running reference, reversed list, {pattern}")
+    got = to_host(_lib.block_sparse_attn_fwd(dq, dk, dv, 128, 64, torch.from_numpy(idx).cuda(),
+                                             torch.from_numpy(cnt).cuda()))
+    ref = oracle.block_sparse_attention(q, k, v, 128, 64, idx, cnt)
+    assert_attn_close(got, ref, what=f"reversed list {pattern}")
 
 
 def test_bf16_deterministic():

@@ -26,7 +26,7 @@ import pytest
 import oracle
 from video_diffusion_transformer_lvsa_amd import _lib, synth
 
-from helpers import attn_errors, note, sample_frame_rows, to_dev, to_host
+from helpers import TILE_OFFSETS, attn_errors, jumping_scores_qkv, note, sample_frame_rows, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -293,6 +293,37 @@ def test_fp8_dense_within_bound(n):
     bound, model = (oracle.dense_attention(dq, dk, dv, fn=f) for f in (oracle.p_rounding_bound, oracle.attention_p_e4m3))
     slack = oracle.dense_attention(dq, dk, dv, fn=_acc_slack)
     _assert_within_bound(got, ref, bound, model, float(np.abs(dv).max()), f"dense n={n}", slack)
+
+
+@pytest.mark.parametrize("pattern", sorted(TILE_OFFSETS))
+def test_fp8_running_reference_moves(pattern):
+    """Scores that jump between 64-key tiles (by up to ~30 bits), so the FP8
+    kernel moves its reference (a lane sum of a tile above 2^8) on many tiles
+    and for a subset of the rows of a wave; every probability stays inside
+    the E4M3 range and the result within the derived bound. Dense (n = 768:
+    8-wave workgroups) walks the keys in order, the reversed block list
+    (128-row query blocks: 4-wave workgroups) backwards."""
+    torch = _torch()
+    heads, ntile, d = 2, 12, 128
+    n = 64 * ntile
+    q, k, v = (synth.bf16_round(x) for x in jumping_scores_qkv(50 + len(pattern), heads, ntile, d, pattern))
+    dev, (dq, dk, dv) = _quant_pair(q, k, v)
+    note(f"fp8 running reference, dense, {pattern}")
+    got = to_host(_run_fp8(dev))
+    ref = oracle.dense_attention(dq, dk, dv)
+    bound, model = (oracle.dense_attention(dq, dk, dv, fn=f) for f in (oracle.p_rounding_bound, oracle.attention_p_e4m3))
+    slack = oracle.dense_attention(dq, dk, dv, fn=_acc_slack)
+    _assert_within_bound(got, ref, bound, model, float(np.abs(dv).max()), f"dense {pattern}", slack)
+    nqb = n // 128
+    idx = np.tile(np.arange(ntile, dtype=np.int32)[::-1], (1, nqb, 1))
+    cnt = np.full((1, nqb), ntile, dtype=np.int32)
+    note(f"fp8 running reference, reversed list, {pattern}")
+    got = to_host(_run_fp8(dev, 128, 64, torch.from_numpy(idx).cuda(), torch.from_numpy(cnt).cuda()))
+    ref = oracle.block_sparse_attention(dq, dk, dv, 128, 64, idx, cnt)
+    bound, model = (oracle.block_sparse_attention(dq, dk, dv, 128, 64, idx, cnt, fn=f)
+                    for f in (oracle.p_rounding_bound, oracle.attention_p_e4m3))
+    slack = oracle.block_sparse_attention(dq, dk, dv, 128, 64, idx, cnt, fn=_acc_slack)
+    _assert_within_bound(got, ref, bound, model, float(np.abs(dv).max()), f"reversed list {pattern}", slack)
 
 
 @pytest.mark.parametrize("T,H,W,heads,C,win,T_per", LVSA_FP8)
