@@ -245,8 +245,9 @@ int quantize_fp8_e4m3(const void* src, int dt, int heads, int n, int d, int tran
  * block_sparse_attn_fwd (Draft: q8/k8/vt8 quantized from the reordered
  * tensors), on the values q = q_scale[h] * decode(q8) (likewise k, v):
  *   s_ij = scale * <q_i, k_j> (exact products, fp32 sums, on the FP8
- *   matrix cores), probabilities exp(s_ij - m) in fp32 with m the running
- *   maximum (updated only when it grows by more than 2^8 in base 2), the
+ *   matrix cores), probabilities exp(s_ij - m) in fp32 with m a score of
+ *   the row that lags its running maximum (moved to the maximum whenever a
+ *   tile's probabilities could exceed 2^8, so every one is <= 2^8), the
  *   probabilities rounded to E4M3 (nearest even) for the PV product, the row
  *   sum over the unrounded fp32 values, O fp32 [heads, n, 128].
  * Requires d = 128, n a multiple of 4, block_k >= 64 and a multiple of 4
