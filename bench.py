@@ -501,8 +501,11 @@ def run_draft(args, w):
                      if fp8 else ("bsa_fwd_d128_kernel<MODE_LIST, true>" if reorder
                                   else "bsa_fwd_d128_kernel<MODE_T2D, false>")},
     }
+    if reorder and sparsity == w.sparsity and pool == "mean":
+        ctr = counters_for(w.name + ("-fp8" if fp8 else ""), ATTN_FP8_SRC if fp8 else ATTN_SRC)
+        if ctr is not None:
+            res["counters"] = ctr
     if not args.no_dense:
-        # dense attention over the unpadded tokens at the same shape
         # dense attention over the unpadded raster tokens at the same shape
         # and arithmetic (FP8 codes of the raster tensors for an FP8 line)
         log("timing dense attention at the same shape")
