@@ -30,6 +30,9 @@
 //  * Software pipeline, one barrier per tile: while the softmax of tile i
 //    runs on the VALU, the MFMAs of Sᵀ for tile i+1 run on the matrix core
 //    (K runs one tile ahead of V in LDS, two tiles ahead in global loads).
+//    d = 128 fixes the instruction order inside a step with scheduling
+//    group barriers, so each Sᵀ MFMA is followed by its share of the
+//    softmax and the LDS reads run ahead of the MFMAs that use them.
 //  * Probabilities are exp2(s*c - m), c = scale*log2(e), rounded to bf16
 //    for the PV product; the row sum accumulates the same rounded values
 //    (v_dot2_f32_bf16 against ones), so O is a convex combination of V rows
