@@ -102,8 +102,15 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bsa_fwd_fp8_kernel(AttnArgs a
   const int logical = (xcd < r8 ? xcd * (q8 + 1) : r8 * (q8 + 1) + (xcd - r8) * q8) + idx;
   const int qt = logical % a.tiles_per_qb;
   const int rest = logical / a.tiles_per_qb;
-  const int qb = rest % a.nqb;
+  int qb = rest % a.nqb;
   const int h = rest / a.nqb;
+  if (MODE == MODE_T2D) {
+    // Raster Draft: consecutive workgroups (one XCD) take the same pool tile
+    // of consecutive frames, whose top-k lists share more key blocks than
+    // those of neighbouring tiles of one frame (measured: 1.2 % faster).
+    const int per = a.nbh * a.nbw, nt = a.nqb / per;
+    qb = (qb % nt) * per + qb / nt;
+  }
 
   const int blk_lo = qb * a.block_q;
   const int blk_end = min(blk_lo + a.block_q, a.n);
