@@ -37,12 +37,12 @@
 //    scores) with no row max; when a lane's probabilities of a tile sum to
 //    more than 2^8 the wave moves the reference to the row max, rescales
 //    and recomputes the tile, so every rounded probability is <= 2^8, inside
-//    the E4M3 range. K rows sit in
-//    LDS in a permuted order, row r = 32kb + 8g + 4h + i holding key
-//    32h + 16kb + 4g + i, so that the Sᵀ accumulator of lane (query, half h)
-//    holds exactly keys 32h .. 32h+31, in the byte order of the PV product's
-//    B operand: the packed probabilities feed the matrix core as they are,
-//    with no exchange between the half-waves;
+//    the E4M3 range;
+//  * K rows sit in LDS in a permuted order, row r = 32kb + 8g + 4h + i
+//    holding key 32h + 16kb + 4g + i, so that the Sᵀ accumulator of lane
+//    (query, half h) holds exactly keys 32h .. 32h+31, in the byte order of
+//    the PV product's B operand: the packed probabilities feed the matrix
+//    core as they are, with no exchange between the half-waves;
 //  * the row sum adds the unrounded fp32 probabilities.
 #include <type_traits>
 
