@@ -174,6 +174,8 @@ int token_permute(const void* src, void* dst, int dt, int heads, int n_src, int 
  * block_q == block_k). A query with no keys gets output 0.
  *   O[h,i,:] = sum_j exp(s_ij - m_i) V[h,j,:] / sum_j exp(s_ij - m_i),
  *   s_ij = scale * <Q[h,i,:], K[h,j,:]>, m_i = max_j s_ij   (not causal).
+ * scale must be finite and > 0 (LVSA_EINVAL otherwise): keys outside the
+ * set enter the kernels as scores of -infinity before the scale is applied.
  * bf16: QKᵀ and PV on bf16 MFMA with fp32 accumulation; probabilities are
  * rounded to bf16 for the PV product and the row sum uses those same rounded
  * values. fp32: fp32 arithmetic throughout. O is fp32 [heads, n, d].

@@ -95,6 +95,9 @@ def test_attention_validation(lib):
     assert call(cnt=None) == _lib.LVSA_EINVAL
     assert call(bv=FAKE, bk=32) == _lib.LVSA_EINVAL
     assert call(scale=float("inf")) == _lib.LVSA_EINVAL
+    assert call(scale=0.0) == _lib.LVSA_EINVAL
+    assert call(scale=-0.088) == _lib.LVSA_EINVAL
+    assert call(scale=float("nan")) == _lib.LVSA_EINVAL
     assert call(n=1 << 23) == _lib.LVSA_EINVAL  # n*d >= 2^30
     # empty problems are valid no-ops
     assert call(heads=0) == 0
@@ -103,6 +106,8 @@ def test_attention_validation(lib):
     assert g(FAKE, FAKE, FAKE, FAKE, 1, 2, 256, 100, 0.1, None) == _lib.LVSA_EUNSUPPORTED
     assert g(FAKE, FAKE, FAKE, None, 1, 2, 256, 128, 0.1, None) == _lib.LVSA_EINVAL
     assert g(FAKE, FAKE, FAKE, FAKE, 1, 0, 256, 128, 0.1, None) == 0
+    for sc in (0.0, -0.1, float("nan")):
+        assert g(FAKE, FAKE, FAKE, FAKE, 1, 2, 256, 128, sc, None) == _lib.LVSA_EINVAL
 
 
 def test_mask_and_permute_validation(lib):
@@ -141,7 +146,9 @@ def test_mask_and_permute_validation(lib):
                          (4, 0, _lib.LVSA_EUNSUPPORTED),    # fp32
                          (10, 4, _lib.LVSA_EUNSUPPORTED),   # 4x16 = 64 slots: fine; pool 4x8 below
                          (14, -1, _lib.LVSA_EINVAL),        # max_kv < 0
-                         (15, float("inf"), _lib.LVSA_EINVAL)]:
+                         (15, float("inf"), _lib.LVSA_EINVAL),
+                         (15, 0.0, _lib.LVSA_EINVAL),        # scale must be positive
+                         (15, -0.088, _lib.LVSA_EINVAL)]:
         bad = list(ok)
         bad[i] = val
         if i == 10:
@@ -191,6 +198,8 @@ def test_fp8_validation(lib):
                          (16, 3, _lib.LVSA_EINVAL),          # mask_heads
                          (15, -1, _lib.LVSA_EINVAL),         # max_kv
                          (18, float("nan"), _lib.LVSA_EINVAL),
+                         (18, 0.0, _lib.LVSA_EINVAL),
+                         (18, -0.088, _lib.LVSA_EINVAL),
                          (4, None, _lib.LVSA_EINVAL),        # q_scale
                          (0, MIS, _lib.LVSA_EINVAL),         # q8 misaligned
                          (14, None, _lib.LVSA_EINVAL)]:      # kv_cnt
@@ -211,6 +220,7 @@ def test_fp8_validation(lib):
                          (3, 118784, _lib.LVSA_EINVAL),      # ldv < n
                          (17, -1, _lib.LVSA_EINVAL),         # max_kv
                          (16, None, _lib.LVSA_EINVAL),       # kv_cnt
+                         (18, 0.0, _lib.LVSA_EINVAL),        # scale
                          (4, None, _lib.LVSA_EINVAL)]:       # q_scale
         bad = list(ok)
         bad[i] = val
@@ -228,6 +238,7 @@ def test_fp8_validation(lib):
     assert dn(*(ok[:3] + [1000] + ok[4:])) == _lib.LVSA_EINVAL
     assert dn(*(ok[:6] + [None] + ok[7:])) == _lib.LVSA_EINVAL
     assert dn(*(ok[:8] + [0] + ok[9:])) == 0
+    assert dn(*(ok[:11] + [-0.088] + ok[12:])) == _lib.LVSA_EINVAL
 
 
 @pytest.mark.skipif(not _no_gpu(), reason="checks the no-device error path")

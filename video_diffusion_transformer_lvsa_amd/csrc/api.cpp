@@ -167,7 +167,7 @@ int check_fp8_attn(const void* q8, const void* k8, const void* vt8, int ldv, con
   if ((long long)n * d >= (1ll << 30)) return fail(LVSA_EINVAL, "n*d=%lld exceeds 2^30", (long long)n * d);
   if (ldv < n || ldv % 16 != 0) return fail(LVSA_EINVAL, "ldv=%d must be a multiple of 16 and >= n=%d", ldv, n);
   if ((long long)d * ldv >= (1ll << 31)) return fail(LVSA_EINVAL, "d*ldv exceeds 2^31");
-  if (!std::isfinite(scale)) return fail(LVSA_EINVAL, "scale must be finite");
+  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(LVSA_EINVAL, "scale must be finite and positive");
   if (heads > 0 && n > 0) {
     if (!q8 || !k8 || !vt8 || !o || !qs || !ks || !vs)
       return fail(LVSA_EINVAL, "q8, k8, vt8, o and the scales must be non-NULL");
@@ -346,7 +346,7 @@ int block_sparse_attn_fwd(const void* q, const void* k, const void* v, float* o,
   if (block_q < 1 || block_k < 1) return fail(LVSA_EINVAL, "block_q=%d block_k=%d must be >= 1", block_q, block_k);
   if (max_kv < 0) return fail(LVSA_EINVAL, "max_kv=%d must be >= 0", max_kv);
   if (mask_heads != 1 && mask_heads != heads) return fail(LVSA_EINVAL, "mask_heads=%d must be 1 or heads=%d", mask_heads, heads);
-  if (!std::isfinite(scale)) return fail(LVSA_EINVAL, "scale must be finite");
+  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(LVSA_EINVAL, "scale must be finite and positive");
   if (block_valid && block_q != block_k) return fail(LVSA_EINVAL, "block_valid requires block_q == block_k");
   if (heads == 0 || n == 0) return LVSA_OK;
   if (!kv_cnt || (max_kv > 0 && !kv_idx)) return fail(LVSA_EINVAL, "kv_cnt (and kv_idx when max_kv > 0) must be non-NULL");
@@ -390,7 +390,7 @@ int draft_attn_fwd(const void* q, const void* k, const void* v, float* o, int dt
     return fail(LVSA_EUNSUPPORTED, "pool %dx%d: pool_h*pool_w must be a multiple of 64 and pool_w must divide 64",
                 pool_h, pool_w);
   if (max_kv < 0) return fail(LVSA_EINVAL, "max_kv=%d must be >= 0", max_kv);
-  if (!std::isfinite(scale)) return fail(LVSA_EINVAL, "scale must be finite");
+  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(LVSA_EINVAL, "scale must be finite and positive");
   if (heads == 0) return LVSA_OK;
   if (!kv_cnt || (max_kv > 0 && !kv_idx)) return fail(LVSA_EINVAL, "kv_cnt (and kv_idx when max_kv > 0) must be non-NULL");
   if ((long long)max_kv * g.bs >= (1ll << 31)) return fail(LVSA_EINVAL, "key list spans more than 2^31 rows");
@@ -437,7 +437,7 @@ int dense_attn_fwd(const void* q, const void* k, const void* v, float* o, int dt
   clear_err();
   int rc = check_attn(q, k, v, o, dt, heads, n, d);
   if (rc) return rc;
-  if (!std::isfinite(scale)) return fail(LVSA_EINVAL, "scale must be finite");
+  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(LVSA_EINVAL, "scale must be finite and positive");
   if (heads == 0 || n == 0) return LVSA_OK;
   lvsa::AttnArgs a{};
   a.q = q;
