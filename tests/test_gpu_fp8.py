@@ -281,6 +281,26 @@ def test_fp8_block_list_edge_cases(k_zero):
         _assert_within_bound(got, ref, bound, model, float(np.abs(dv).max()), "edge lists", slack)
 
 
+def test_fp8_tiny_scores_stay_finite():
+    """Q and K of magnitude 1e-21: the per-head scales multiply to less than
+    the smallest fp32 subnormal, so every score is 0 to within fp32 and the
+    result is the mean of V over each key set -- partial tiles included (a
+    short last block, skipped list entries, an empty list), where a masked
+    key must still weigh 0 (not NaN)."""
+    torch = _torch()
+    rng = np.random.default_rng(21)
+    heads, n, d, bq, bk, max_kv = 2, 700, 128, 128, 96, 5
+    q, k = (synth.bf16_round(rng.standard_normal((heads, n, d)).astype(np.float32) * np.float32(1e-21))
+            for _ in range(2))
+    v = _integer_v(rng, heads, n, d)
+    idx, cnt, clean, ccnt = _edge_lists(rng, heads, n, bq, bk, max_kv)
+    note("fp8 tiny scores")
+    dev, (dq, dk, dv) = _quant_pair(q, k, v)
+    got = to_host(_run_fp8(dev, bq, bk, torch.from_numpy(idx).cuda(), torch.from_numpy(cnt).cuda(), mask_heads=heads))
+    ref = oracle.block_sparse_attention(dq, dk, dv, bq, bk, clean, ccnt, mask_heads=heads)
+    _assert_exact_mean(got, ref, "tiny scores")
+
+
 @pytest.mark.parametrize("n", DENSE_N)
 def test_fp8_dense_within_bound(n):
     rng = np.random.default_rng(100 + n)

@@ -286,7 +286,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bsa_fwd_fp8_kernel(AttnArgs a
     for (int r = 0; r < 16; ++r) oacc[i][r] = 0.f;
   float mc = -INFINITY;
   float l_run = 0.f;
-  const float c = a.scale_log2 * qsc[h] * ksc[h];
+  // Kept a positive normal number: with tiny per-head scales the product
+  // could underflow to 0, and a masked key's -inf score times 0 is NaN. At
+  // that size every score is 0 to within fp32, so the result is unchanged.
+  const float c = fmaxf(a.scale_log2 * qsc[h] * ksc[h], 1.17549435e-38f);
 
   // exp2(s*c - m) of a tile's scores in E4M3 as the Pᵀ operand: word
   // 4kb + g holds the scores cur[kb][4g .. 4g+3], keys 32*half + 16kb + 4g +
