@@ -176,6 +176,8 @@ int token_permute(const void* src, void* dst, int dt, int heads, int n_src, int 
  *   s_ij = scale * <Q[h,i,:], K[h,j,:]>, m_i = max_j s_ij   (not causal).
  * scale must be finite and > 0 (LVSA_EINVAL otherwise): keys outside the
  * set enter the kernels as scores of -infinity before the scale is applied.
+ * Inputs whose fp32 dot products overflow (|<q, k>| above ~3.4e38) are
+ * outside the domain: their rows come out NaN.
  * bf16: QKᵀ and PV on bf16 MFMA with fp32 accumulation; probabilities are
  * rounded to bf16 for the PV product and the row sum uses those same rounded
  * values. fp32: fp32 arithmetic throughout. O is fp32 [heads, n, d].
