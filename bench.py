@@ -18,6 +18,7 @@ oracle is timed on a bounded sample as a reported baseline.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import math
@@ -139,7 +140,7 @@ def cpu_baseline_lvsa(w, q, k, v, budget_s: float):
         "unit": "TFLOP/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": f"{done} (head, query-frame) pairs of 1560 rows x {w.C} frames of keys, LVSA s=0, fp64 numpy, "
+        "sample": f"{done} (head, query-frame) pairs of {w.P} rows x {w.C} frames of keys, LVSA s=0, fp64 numpy, "
                   f"{dt:.1f} s",
         "seconds": dt,
         "ms_per_call_extrapolated": dt / pairs * (lvsa_pairs(w, cnt)) * 1e3,
@@ -214,6 +215,7 @@ def run_lvsa(args, w):
 
     from video_diffusion_transformer_lvsa_amd import _lib, synth
 
+    own_budget = w.C == synth.WORKLOADS[w.name].C
     log(f"generating inputs for {w.name}")
     q, k, v = synth.video_qkv(w.seed, w.heads, w.T, w.H, w.W, w.d)
     dev = torch.device("cuda:0")
@@ -316,7 +318,7 @@ def run_lvsa(args, w):
         "dtype": "fp8-e4m3" if fp8 else "bf16",
         "data": "synthetic",
         "config": {
-            "workload": WORKLOAD_NAMES[w.name] + ("-fp8" if fp8 else ""),
+            "workload": WORKLOAD_NAMES[w.name] + ("" if own_budget else f"-C{w.C}") + ("-fp8" if fp8 else ""),
             "T": w.T, "H": w.H, "W": w.W, "tokens": w.N, "heads": w.heads, "d": w.d,
             "C": w.C, "window": w.window, "T_per": w.T_per, "steps_s": "s = step mod T_per",
             "flop_per_call": flop_per_launch,
@@ -336,10 +338,12 @@ def run_lvsa(args, w):
         "peak": peak,
         "unit": "TFLOP/s",
         "frac": round(achieved / peak, 4),
-        "traffic": traffic_for(w.name + ("-fp8" if fp8 else ""), ATTN_FP8_SRC if fp8 else ATTN_SRC),
+        # the counter records were taken at the workload's own frame budget
+        "traffic": traffic_for(w.name + ("-fp8" if fp8 else ""), ATTN_FP8_SRC if fp8 else ATTN_SRC)
+        if own_budget else None,
         "kernel": "bsa_fwd_fp8_kernel<MODE_LIST, 4>" if fp8 else "bsa_fwd_d128_kernel<MODE_LIST, false>",
     }
-    ctr = counters_for(w.name + ("-fp8" if fp8 else ""), ATTN_FP8_SRC if fp8 else ATTN_SRC)
+    ctr = counters_for(w.name + ("-fp8" if fp8 else ""), ATTN_FP8_SRC if fp8 else ATTN_SRC) if own_budget else None
     if ctr is not None:
         res["counters"] = ctr
 
@@ -716,6 +720,7 @@ def main(argv=None) -> int:
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--sparsity", type=float, default=None, help="Draft workload: override the 90%% sparsity")
+    ap.add_argument("--budget", type=int, default=None, help="LVSA workloads: override the frame budget C")
     ap.add_argument("--pool", choices=("mean", "max"), default="mean", help="Draft workload: pooling of Q and K")
     ap.add_argument("--no-reorder", action="store_true",
                     help="Draft workload: attend on the raster layout (draft_attn_fwd) instead of reordering")
@@ -744,6 +749,11 @@ def main(argv=None) -> int:
     if args.calib_copy_mb > 0:
         calibrate_copy(args.calib_copy_mb)
     w = synth.WORKLOADS[args.workload]
+    if args.budget is not None and w.kind == "lvsa":
+        if args.budget < 1:
+            print("--budget must be at least 1", file=sys.stderr)
+            return 2
+        w = dataclasses.replace(w, C=args.budget)
     res = run_draft(args, w) if w.kind == "draft" else run_lvsa(args, w)
     print(json.dumps(res), flush=True)
     return 0

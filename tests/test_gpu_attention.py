@@ -134,6 +134,7 @@ def test_bf16_block_list_edge_cases():
     (640, 130, 64, 5, 2, False),    # 2-row last tiles
     (1560 * 3, 1560, 1560, 3, 1, True),
     (900, 300, 100, 200, 2, False),  # long lists
+    (1000, 150, 250, 12, 1, False),  # 4 KV blocks: neighbours share entries at other multiplicities
 ])
 def test_bf16_ragged_query_blocks(n, bq, bk, max_kv, mask_heads, sorted_lists):
     """Query blocks that end in a partial 128-row tile, with unsorted lists,
