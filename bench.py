@@ -738,9 +738,18 @@ def main(argv=None) -> int:
               "no exchange; see the design notes). Run with --gpus 1.", file=sys.stderr)
         return 2
 
+    from video_diffusion_transformer_lvsa_amd import synth
+
+    w = synth.WORKLOADS[args.workload]
+    if args.budget is not None:
+        if w.kind != "lvsa" or args.budget < 1:
+            print("--budget takes a frame count >= 1 and applies to the LVSA workloads only", file=sys.stderr)
+            return 2
+        w = dataclasses.replace(w, C=args.budget)
+
     import torch
 
-    from video_diffusion_transformer_lvsa_amd import _lib, synth
+    from video_diffusion_transformer_lvsa_amd import _lib
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -748,12 +757,6 @@ def main(argv=None) -> int:
     _lib.load()
     if args.calib_copy_mb > 0:
         calibrate_copy(args.calib_copy_mb)
-    w = synth.WORKLOADS[args.workload]
-    if args.budget is not None and w.kind == "lvsa":
-        if args.budget < 1:
-            print("--budget must be at least 1", file=sys.stderr)
-            return 2
-        w = dataclasses.replace(w, C=args.budget)
     res = run_draft(args, w) if w.kind == "draft" else run_lvsa(args, w)
     print(json.dumps(res), flush=True)
     return 0

@@ -39,6 +39,13 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode == 2 and "one GPU" in r.stderr
 
 
+@pytest.mark.parametrize("extra", [["--budget", "0"], ["--workload", "hunyuan-draft", "--budget", "8"]])
+def test_bad_frame_budget_is_refused(extra):
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py")] + extra, capture_output=True, text=True,
+                       cwd=ROOT)
+    assert r.returncode == 2 and "--budget" in r.stderr
+
+
 def test_traffic_summary_scales_by_the_copy_calibration(tmp_path):
     mib = 64
     rows = mib * (1 << 20) // 256
