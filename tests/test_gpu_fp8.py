@@ -375,15 +375,25 @@ def test_fp8_deterministic():
 
 def test_full_wan13b_6x_lvsa_fp8():
     """Wan2.1-1.3B at 6x length (126 frames of 1560 tokens, 12 heads), the
-    LVSA mask at two steps; quantizer codes checked on two heads, attention on
-    sampled rows of three heads against the oracle on the dequantized values."""
+    LVSA mask at two steps; quantizer codes checked on three heads, attention
+    on sampled rows of those heads against the oracle on the dequantized
+    values."""
+    _full_lvsa_fp8("wan1.3b-6x", [0, 5, 11], (0, 3))
+
+
+def test_full_hunyuan_lvsa_fp8():
+    """The HunyuanVideo-shaped LVSA workload at 1.5x length (24 heads), as
+    the Wan test above: the configuration whose FP8 time is reported."""
+    _full_lvsa_fp8("hunyuan-lvsa-1.5x", [0, 11, 23], (0, 5))
+
+
+def _full_lvsa_fp8(name, heads, steps):
     torch = _torch()
-    w = synth.WORKLOADS["wan1.3b-6x"]
+    w = synth.WORKLOADS[name]
     q, k, v = synth.video_qkv(w.seed, w.heads, w.T, w.H, w.W, w.d)
-    note("wan1.3b-6x fp8 quantize")
+    note(f"{name} fp8 quantize")
     dev = _lib.quantize_qkv_fp8(to_dev(q), to_dev(k), to_dev(v))
     torch.cuda.synchronize()
-    heads = [0, 5, 11]
     deq = []
     for name, x, tr in (("q8", q, False), ("k8", k, False), ("vt8", v, True)):
         c, s = oracle.quantize_per_head(synth.bf16_to_f32(x[heads]), transpose=tr)
@@ -396,10 +406,10 @@ def test_full_wan13b_6x_lvsa_fp8():
         deq.append(oracle.dequantize(c, s, transposed=tr))
     dq, dk, dv = deq
     vmax = float(np.abs(dv).max())
-    for s in (0, 3):
+    for s in steps:
         rng = np.random.default_rng(700 + s)
         rows = sample_frame_rows(rng, w.T, w.P, nframes=4, per_frame=48)
-        note(f"wan1.3b-6x fp8 lvsa s={s}")
+        note(f"{name} fp8 lvsa s={s}")
         idx, cnt = _lib.lvsa_mask(w.T, w.C, w.window, w.T_per, s)
         o = _run_fp8(dev, w.P, w.P, idx, cnt)
         got = to_host(o[heads])[:, rows]
@@ -408,7 +418,7 @@ def test_full_wan13b_6x_lvsa_fp8():
         bound, model = (oracle.block_sparse_attention(dq, dk, dv, w.P, w.P, want_idx, want_cnt, rows=rows, fn=f)
                         for f in (oracle.p_rounding_bound, oracle.attention_p_e4m3))
         slack = oracle.block_sparse_attention(dq, dk, dv, w.P, w.P, want_idx, want_cnt, rows=rows, fn=_acc_slack)
-        _assert_within_bound(got, ref, bound, model, vmax, f"wan1.3b-6x fp8 s={s}", slack)
+        _assert_within_bound(got, ref, bound, model, vmax, f"{name} fp8 s={s}", slack)
         del o
     del dev
     torch.cuda.empty_cache()
