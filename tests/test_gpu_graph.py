@@ -111,3 +111,31 @@ def test_graph_draft_raster_step():
         _lib.draft_attn_fwd(q, k, v, T, H, W, ph, pw, kv_idx, kv_cnt, out=o)
 
     _replay_and_check(step, [kv_idx, kv_cnt, o], "draft raster step")
+
+
+def test_graph_draft_reorder_step():
+    """The Draft step as the article lays it out: mask and reorder, block-
+    sparse attention on the reordered tensors, scatter back to token order."""
+    torch = _torch()
+    T, H, W, ph, pw, heads, sp = 3, 45, 80, 8, 16, 2, 0.9
+    q, k, v = (to_dev(x) for x in synth.video_qkv(7, heads, T, H, W, 128))
+    info = _lib.draft_grid_info(T, H, W, ph, pw, sp)
+    nb, n_pad, n, bs = info["nb"], info["n_pad"], T * H * W, ph * pw
+    i32 = dict(dtype=torch.int32, device="cuda")
+    bufs = {"kv_idx": torch.empty((heads, nb, info["k"]), **i32), "kv_cnt": torch.empty((heads, nb), **i32),
+            "perm": torch.empty((n_pad,), **i32), "inv_perm": torch.empty((n,), **i32),
+            "block_valid": torch.empty((nb,), **i32),
+            "workspace": torch.empty((_lib.draft_workspace_bytes(heads, T, H, W, 128, ph, pw) // 4,),
+                                     dtype=torch.float32, device="cuda")}
+    for name in ("q_perm", "k_perm", "v_perm"):
+        bufs[name] = torch.empty((heads, n_pad, 128), dtype=q.dtype, device="cuda")
+    o_perm = torch.empty((heads, n_pad, 128), dtype=torch.float32, device="cuda")
+    o = torch.empty((heads, n, 128), dtype=torch.float32, device="cuda")
+
+    def step():
+        _lib.draft_mask_and_perm(q, k, v, T, H, W, ph, pw, sp, buffers=bufs)
+        _lib.block_sparse_attn_fwd(bufs["q_perm"], bufs["k_perm"], bufs["v_perm"], bs, bs, bufs["kv_idx"],
+                                   bufs["kv_cnt"], mask_heads=heads, block_valid=bufs["block_valid"], out=o_perm)
+        _lib.token_permute(o_perm, bufs["inv_perm"], out=o)
+
+    _replay_and_check(step, [bufs["kv_idx"], bufs["q_perm"], o_perm, o], "draft reorder step")
