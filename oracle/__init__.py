@@ -24,8 +24,11 @@ Sources (cited by page title and section):
   that makes the kept blocks contiguous.
 
 Every function is pinned by ``tests/test_oracle_*.py`` (``-m "not gpu"``)
-against closed forms, invariants, brute force and a library routine; none is
-"parity unpinned".
+against closed forms, invariants, brute force and a library routine,
+including the bfloat16 decode ``to_f64`` (fixed bit patterns, all 65536
+codes against a decoder written from the format's fields, torch's own
+conversion). The FP8 probability rounding is pinned by a derived bound and
+a statistical match rather than element by element.
 """
 from .lvsa import anchors, nearest_order, attend_set, lvsa_mask, lvsa_capacity
 from .draft import (

@@ -88,3 +88,20 @@ def jumping_scores_qkv(seed: int, heads: int, ntile: int, d: int, pattern: str):
     q[:, :, 0] = 8.0 * rng.uniform(0.05, 1.0, size=(heads, n)).astype(np.float32)
     k[:, :, 0] += np.repeat(TILE_OFFSETS[pattern](ntile), 64).astype(np.float32)[None, :]
     return q, k, v
+
+
+def bf16_decode_fields(bits) -> np.ndarray:
+    """bfloat16 bit patterns -> float64 from the format's field definition
+    (1 sign bit, 8 exponent bits with bias 127, 7 fraction bits; exponent 0
+    is zero or subnormal with scale 2^-126, exponent 255 is infinity or NaN),
+    computed with integer fields and ldexp rather than a bit shift, so it
+    checks the oracle's decode by a different route."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.int64)
+    sign = np.where((b >> 15) & 1, -1.0, 1.0)
+    e = (b >> 7) & 0xFF
+    m = (b & 0x7F).astype(np.float64)
+    normal = np.ldexp(1.0 + m / 128.0, (e - 127).astype(np.int32))
+    sub = np.ldexp(m / 128.0, -126)
+    special = np.where(m == 0, np.inf, np.nan)
+    mag = np.where(e == 0, sub, np.where(e == 255, special, normal))
+    return sign * mag

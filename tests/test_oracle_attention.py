@@ -8,7 +8,15 @@ import pytest
 import torch
 
 import oracle
+from helpers import bf16_decode_fields
 from video_diffusion_transformer_lvsa_amd import synth
+
+
+def _f64(x):
+    """Inputs for the library cross-checks, decoded apart from the oracle:
+    bf16 bit patterns through the field-definition decoder, floats by a cast."""
+    x = np.asarray(x)
+    return bf16_decode_fields(x) if x.dtype == np.uint16 else x.astype(np.float64)
 
 
 def _py_attention(q, k, v, keys, scale):
@@ -38,7 +46,7 @@ def test_brute_force_tiny():
 
 def _sdpa_masked(q, k, v, allowed):
     """torch fp64 SDPA with a boolean [n, n] mask (True = attend)."""
-    qt, kt, vt = (torch.from_numpy(oracle.to_f64(x)) for x in (q, k, v))
+    qt, kt, vt = (torch.from_numpy(_f64(x)) for x in (q, k, v))
     return torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=torch.from_numpy(allowed)).numpy()
 
 
@@ -149,9 +157,9 @@ def test_lvsa_frame_gather_equals_dense_on_gathered_frames():
     got = oracle.block_sparse_attention(q, k, v, P, P, idx, cnt)
     for t in range(T):
         cols = np.concatenate([np.arange(f * P, (f + 1) * P) for f in idx[t, : cnt[t]]])
-        qt = torch.from_numpy(oracle.to_f64(q)[:, t * P : (t + 1) * P])
-        kt = torch.from_numpy(oracle.to_f64(k)[:, cols])
-        vt = torch.from_numpy(oracle.to_f64(v)[:, cols])
+        qt = torch.from_numpy(_f64(q)[:, t * P : (t + 1) * P])
+        kt = torch.from_numpy(_f64(k)[:, cols])
+        vt = torch.from_numpy(_f64(v)[:, cols])
         want = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt).numpy()
         assert np.allclose(got[:, t * P : (t + 1) * P], want, rtol=1e-11, atol=1e-12)
 

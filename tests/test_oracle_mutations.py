@@ -15,6 +15,7 @@ import oracle.draft as D
 import oracle.fp8 as F
 import oracle.lvsa as L
 import test_oracle_attention as TA
+import test_oracle_bf16 as TB
 import test_oracle_draft as TD
 import test_oracle_fp8 as TF
 import test_oracle_lvsa as TL
@@ -149,6 +150,15 @@ def _attend_no_expansion(real):
     return attend
 
 
+def _to_f64_shift8(real):
+    def to_f64(x):
+        x = np.asarray(x)
+        if x.dtype == np.uint16:
+            return (x.astype(np.uint32) << np.uint32(8)).view(np.float32).astype(np.float64)
+        return real(x)
+    return to_f64
+
+
 def _anchors_shifted(real):
     return lambda T, T_per, s: real(T, T_per, (s + 1) % T_per)
 
@@ -179,6 +189,9 @@ MUTATIONS = [
      lambda gd: [lambda: TA.test_lvsa_tiny_vs_sdpa(1), TA.test_full_mask_equals_dense]),
     ("LVSA window never widened", L, "attend_set", _attend_no_expansion,
      lambda gd: [lambda: TL.test_worked_examples(gd)]),
+    ("bf16 decode shifts by 8 instead of 16", A, "to_f64", _to_f64_shift8,
+     lambda gd: [TB.test_fixed_patterns, TA.test_lvsa_frame_gather_equals_dense_on_gathered_frames,
+                 TA.test_draft_reorder_invariance]),
     ("LVSA anchors one step off", L, "anchors", _anchors_shifted,
      lambda gd: [lambda: TL.test_worked_examples(gd)]),
 ]
