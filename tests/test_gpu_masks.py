@@ -36,6 +36,26 @@ def test_lvsa_mask_extra_capacity_is_padded():
     assert np.array_equal(to_host(idx), want_idx) and np.all(to_host(idx)[:, 21:] == -1)
 
 
+def test_lvsa_mask_reused_max_cap_buffer():
+    """One buffer sized for the largest step's capacity, reused across steps
+    without passing cap: the lists are written at the buffer's row pitch
+    (capacity differs by step: T=10, C=3, W=2, T_per=4 needs 5, 5, 4, 4)."""
+    import torch
+
+    T, C, W, T_per = 10, 3, 2, 4
+    caps = [_lib.lvsa_mask_capacity(T, C, W, T_per, s) for s in range(T_per)]
+    assert len(set(caps)) > 1
+    cap = max(caps)
+    idx = torch.full((T, cap), 123, dtype=torch.int32, device="cuda")
+    cnt = torch.empty((T,), dtype=torch.int32, device="cuda")
+    for s in list(range(T_per)) * 2:
+        note(f"lvsa_mask reused buffer s={s}")
+        _lib.lvsa_mask(T, C, W, T_per, s, kv_idx=idx, kv_cnt=cnt)
+        want_idx, want_cnt = oracle.lvsa_mask(T, C, W, T_per, s, cap=cap)
+        assert np.array_equal(to_host(cnt), want_cnt)
+        assert np.array_equal(to_host(idx), want_idx)
+
+
 DRAFT_CASES = [
     # T, H, W, pool_h, pool_w, heads, d, sparsity, dtype
     (1, 3, 4, 2, 2, 1, 64, 0.5, "f32"),

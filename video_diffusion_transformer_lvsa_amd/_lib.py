@@ -120,6 +120,51 @@ def _contig_cuda(*ts):
             raise ValueError("tensors must be contiguous CUDA (HIP) tensors")
 
 
+def _expect(t, name: str, shape=None, dtype=None, device=None, numel=None, min_numel=None):
+    """Raise ValueError unless tensor t has the given shape, dtype, device and size.
+    The kernels size their index ranges from the scalar arguments, so a tensor
+    that disagrees with them would be read or written out of bounds."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name}: expected dtype {dtype}, got {t.dtype}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name}: expected {numel} elements, got {t.numel()}")
+    if min_numel is not None and t.numel() < min_numel:
+        raise ValueError(f"{name}: expected at least {min_numel} elements, got {t.numel()}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name}: expected device {device}, got {t.device}")
+
+
+def _check_qkv(q, k, v, out=None, what="q"):
+    """q [heads, n, d] and k, v of the same shape, dtype and device; out fp32 [heads, n, d]."""
+    torch = _torch()
+    if q.dim() != 3:
+        raise ValueError(f"{what}: expected [heads, n, d], got shape {tuple(q.shape)}")
+    for name, t in (("k", k), ("v", v)):
+        _expect(t, name, q.shape, q.dtype, q.device)
+    if out is not None:
+        _expect(out, "out", q.shape, torch.float32, q.device)
+
+
+def _check_lists(kv_idx, kv_cnt, lead: tuple, device, kv_idx_required: bool = True):
+    """kv_idx int32 [*lead, max_kv] and kv_cnt int32 [*lead] (a leading 1 may be dropped)."""
+    torch = _torch()
+    _expect(kv_cnt, "kv_cnt", dtype=torch.int32, device=device, numel=math.prod(lead))
+    if kv_idx is None:
+        if kv_idx_required:
+            raise ValueError("kv_idx is required")
+        return 0
+    _expect(kv_idx, "kv_idx", dtype=torch.int32, device=device)
+    got = tuple(kv_idx.shape[:-1])
+    ok = got == tuple(lead) or (len(lead) > 1 and lead[0] == 1 and got == tuple(lead[1:]))
+    if kv_idx.dim() < 2 or not ok:
+        raise ValueError(f"kv_idx: expected shape {tuple(lead)} + (max_kv,), got {tuple(kv_idx.shape)}")
+    return int(kv_idx.shape[-1])
+
+
 def lvsa_mask_capacity(T: int, C: int, window: int, T_per: int, step: int) -> int:
     rc = load().lvsa_mask_capacity(T, C, window, T_per, step)
     if rc < 0:
@@ -131,12 +176,21 @@ def lvsa_mask(T: int, C: int, window: int, T_per: int, step: int, cap: int | Non
               device="cuda", stream=None):
     """LVSA frame lists on the GPU: (kv_idx [T, cap] int32, kv_cnt [T] int32)."""
     torch = _torch()
-    if cap is None:
+    if kv_idx is not None:
+        # the lists are written at the buffer's row pitch, which the attention reads back
+        if kv_idx.dim() != 2 or kv_idx.shape[0] != T:
+            raise ValueError(f"kv_idx: expected shape ({T}, cap), got {tuple(kv_idx.shape)}")
+        if cap is not None and cap != kv_idx.shape[1]:
+            raise ValueError(f"cap={cap} differs from kv_idx's row length {kv_idx.shape[1]}")
+        cap = int(kv_idx.shape[1])
+        _expect(kv_idx, "kv_idx", dtype=torch.int32)
+    elif cap is None:
         cap = lvsa_mask_capacity(T, C, window, T_per, step)
     if kv_idx is None:
         kv_idx = torch.empty((T, cap), dtype=torch.int32, device=device)
     if kv_cnt is None:
-        kv_cnt = torch.empty((T,), dtype=torch.int32, device=device)
+        kv_cnt = torch.empty((T,), dtype=torch.int32, device=kv_idx.device)
+    _expect(kv_cnt, "kv_cnt", (T,), torch.int32, kv_idx.device)
     _contig_cuda(kv_idx, kv_cnt)
     _check(load().lvsa_mask(T, C, window, T_per, step, _ptr(kv_idx), _ptr(kv_cnt), cap, _stream(stream)))
     return kv_idx, kv_cnt
@@ -167,7 +221,12 @@ def draft_mask_and_perm(q, k, v, T: int, H: int, grid_w: int, pool_h: int, pool_
     (float32, draft_workspace_bytes / 4 elements), preallocated by the caller
     (for instance for a captured graph); the others are allocated."""
     torch = _torch()
+    _check_qkv(q, k, v)
     heads, n, d = q.shape
+    if n != T * H * grid_w:
+        raise ValueError(f"q has {n} tokens; the grid {T}x{H}x{grid_w} has {T * H * grid_w}")
+    if pool not in POOL_MODES:
+        raise ValueError(f"pool must be one of {sorted(POOL_MODES)}")
     _contig_cuda(q, k, v)
     info = draft_grid_info(T, H, grid_w, pool_h, pool_w, sparsity)
     nb, n_pad, topk = info["nb"], info["n_pad"], info["k"]
@@ -181,6 +240,7 @@ def draft_mask_and_perm(q, k, v, T: int, H: int, grid_w: int, pool_h: int, pool_
             return torch.empty(shape, **kw)
         if tuple(t.shape) != tuple(shape) or t.dtype != kw["dtype"]:
             raise ValueError(f"{name}: expected {kw['dtype']} {tuple(shape)}, got {t.dtype} {tuple(t.shape)}")
+        _expect(t, name, device=dev)
         return t
 
     out = {
@@ -209,9 +269,13 @@ def draft_mask_and_perm(q, k, v, T: int, H: int, grid_w: int, pool_h: int, pool_
 
 def draft_scores(qbar, kbar, stream=None):
     torch = _torch()
-    _contig_cuda(qbar, kbar)
+    if qbar.dim() != 3 or kbar.dim() != 3:
+        raise ValueError("qbar and kbar must be [heads, nb, d]")
     heads, nbq, d = qbar.shape
     nbk = kbar.shape[1]
+    _expect(qbar, "qbar", dtype=torch.float32)
+    _expect(kbar, "kbar", (heads, nbk, d), torch.float32, qbar.device)
+    _contig_cuda(qbar, kbar)
     s = torch.empty((heads, nbq, nbk), dtype=torch.float32, device=qbar.device)
     _check(load().draft_scores(_ptr(qbar), _ptr(kbar), heads, nbq, nbk, d, _ptr(s), _stream(stream)))
     return s
@@ -220,10 +284,14 @@ def draft_scores(qbar, kbar, stream=None):
 def token_permute(src, dst_to_src, out=None, stream=None):
     """out[h, i] = src[h, dst_to_src[i]] (zeros where the map is -1)."""
     torch = _torch()
+    if src.dim() != 3 or dst_to_src.dim() != 1:
+        raise ValueError("src must be [heads, n_src, d] and dst_to_src one-dimensional")
     heads, n_src, d = src.shape
     n_dst = dst_to_src.shape[0]
+    _expect(dst_to_src, "dst_to_src", dtype=torch.int32, device=src.device)
     if out is None:
         out = torch.empty((heads, n_dst, d), dtype=src.dtype, device=src.device)
+    _expect(out, "out", (heads, n_dst, d), src.dtype, src.device)
     _contig_cuda(src, dst_to_src, out)
     _check(load().token_permute(_ptr(src), _ptr(out), _dt(src), heads, n_src, n_dst, d, _ptr(dst_to_src),
                                 _stream(stream)))
@@ -234,11 +302,18 @@ def block_sparse_attn_fwd(q, k, v, block_q: int, block_k: int, kv_idx, kv_cnt, m
                           scale: float | None = None, out=None, stream=None):
     """Block-sparse attention; returns O fp32 [heads, n, d]."""
     torch = _torch()
+    _check_qkv(q, k, v, out)
     heads, n, d = q.shape
+    if mask_heads not in (1, heads):
+        raise ValueError(f"mask_heads={mask_heads} must be 1 or heads={heads}")
+    if block_q < 1 or block_k < 1:
+        raise ValueError("block_q and block_k must be >= 1")
+    max_kv = _check_lists(kv_idx, kv_cnt, (mask_heads, -(-n // block_q)), q.device)
+    if block_valid is not None:
+        _expect(block_valid, "block_valid", dtype=torch.int32, device=q.device, min_numel=-(-n // block_k))
     if out is None:
         out = torch.empty((heads, n, d), dtype=torch.float32, device=q.device)
     _contig_cuda(q, k, v, out, kv_idx, kv_cnt, block_valid)
-    max_kv = kv_idx.shape[-1]
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     _check(load().block_sparse_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _dt(q), heads, n, d, block_q, block_k,
                                         _ptr(kv_idx), _ptr(kv_cnt), max_kv, mask_heads, _ptr(block_valid), scale,
@@ -249,6 +324,7 @@ def block_sparse_attn_fwd(q, k, v, block_q: int, block_k: int, kv_idx, kv_cnt, m
 def dense_attn_fwd(q, k, v, scale: float | None = None, out=None, stream=None):
     """Dense attention; returns O fp32 [heads, n, d]."""
     torch = _torch()
+    _check_qkv(q, k, v, out)
     heads, n, d = q.shape
     if out is None:
         out = torch.empty((heads, n, d), dtype=torch.float32, device=q.device)
@@ -258,12 +334,24 @@ def dense_attn_fwd(q, k, v, scale: float | None = None, out=None, stream=None):
     return out
 
 
+def _draft_blocks(n: int, T: int, H: int, grid_w: int, pool_h: int, pool_w: int) -> int:
+    """Pool tiles of the grid (raster order), after checking the grid matches n tokens."""
+    if n != T * H * grid_w:
+        raise ValueError(f"{n} tokens; the grid {T}x{H}x{grid_w} has {T * H * grid_w}")
+    if pool_h < 1 or pool_w < 1:
+        raise ValueError("pool sizes must be >= 1")
+    return T * (-(-H // pool_h)) * (-(-grid_w // pool_w))
+
+
 def draft_attn_fwd(q, k, v, T: int, H: int, grid_w: int, pool_h: int, pool_w: int, kv_idx, kv_cnt,
                    scale: float | None = None, out=None, stream=None):
     """Draft attention on the raster layout (no reorder): q, k, v [heads, T*H*grid_w, 128]
     bf16, per-head lists kv_idx [heads, nb, k], kv_cnt [heads, nb]; returns O fp32."""
     torch = _torch()
+    _check_qkv(q, k, v, out)
     heads, n, d = q.shape
+    nb = _draft_blocks(n, T, H, grid_w, pool_h, pool_w)
+    _check_lists(kv_idx, kv_cnt, (heads, nb), q.device)
     if out is None:
         out = torch.empty((heads, n, d), dtype=torch.float32, device=q.device)
     _contig_cuda(q, k, v, out, kv_idx, kv_cnt)
@@ -287,9 +375,12 @@ def quantize_fp8_e4m3(x, transpose: bool = False, ld: int | None = None, out=Non
     codes uint8 [heads, n, d], or [heads, d, ld] when transpose (ld defaults to
     fp8_pitch(n)); scales fp32 [heads] (the value of a code is decode(code) * scale)."""
     torch = _torch()
+    if x.dim() != 3:
+        raise ValueError(f"x: expected [heads, n, d], got shape {tuple(x.shape)}")
     heads, n, d = x.shape
     if transpose:
-        ld = fp8_pitch(n) if ld is None else ld
+        if ld is None:
+            ld = fp8_pitch(n) if out is None else int(out.shape[-1])
         shape = (heads, d, ld)
     else:
         ld = 0
@@ -298,6 +389,8 @@ def quantize_fp8_e4m3(x, transpose: bool = False, ld: int | None = None, out=Non
         out = torch.empty(shape, dtype=torch.uint8, device=x.device)
     if scales is None:
         scales = torch.empty((heads,), dtype=torch.float32, device=x.device)
+    _expect(out, "out", shape, torch.uint8, x.device)
+    _expect(scales, "scales", dtype=torch.float32, device=x.device, numel=heads)
     _contig_cuda(x, out, scales)
     _check(load().quantize_fp8_e4m3(_ptr(x), _dt(x), heads, n, d, int(transpose), ld, _ptr(out), _ptr(scales),
                                     _stream(stream)))
@@ -312,12 +405,37 @@ def quantize_qkv_fp8(q, k, v, stream=None) -> dict:
     return {"q8": q8, "k8": k8, "vt8": vt8, "q_scale": qs, "k_scale": ks, "v_scale": vs}
 
 
+def _check_fp8(q8, k8, vt8, q_scale, k_scale, v_scale, out):
+    """q8, k8 uint8 [heads, n, d]; vt8 uint8 [heads, d, ldv] with ldv >= n; scales fp32 [heads]; out fp32."""
+    torch = _torch()
+    if q8.dim() != 3:
+        raise ValueError(f"q8: expected [heads, n, d], got shape {tuple(q8.shape)}")
+    heads, n, d = q8.shape
+    _expect(q8, "q8", dtype=torch.uint8)
+    _expect(k8, "k8", q8.shape, torch.uint8, q8.device)
+    _expect(vt8, "vt8", dtype=torch.uint8, device=q8.device)
+    if vt8.dim() != 3 or vt8.shape[0] != heads or vt8.shape[1] != d or vt8.shape[2] < n:
+        raise ValueError(f"vt8: expected [{heads}, {d}, ldv >= {n}], got {tuple(vt8.shape)}")
+    for name, t in (("q_scale", q_scale), ("k_scale", k_scale), ("v_scale", v_scale)):
+        _expect(t, name, dtype=torch.float32, device=q8.device, numel=heads)
+    if out is not None:
+        _expect(out, "out", q8.shape, torch.float32, q8.device)
+
+
 def block_sparse_attn_fwd_fp8(q8, k8, vt8, q_scale, k_scale, v_scale, block_q: int, block_k: int, kv_idx, kv_cnt,
                               mask_heads: int = 1, block_valid=None, scale: float | None = None, out=None,
                               stream=None):
     """Block-sparse attention on E4M3 codes (vt8 [heads, 128, ldv]); returns O fp32 [heads, n, 128]."""
     torch = _torch()
+    _check_fp8(q8, k8, vt8, q_scale, k_scale, v_scale, out)
     heads, n, d = q8.shape
+    if mask_heads not in (1, heads):
+        raise ValueError(f"mask_heads={mask_heads} must be 1 or heads={heads}")
+    if block_q < 1 or block_k < 1:
+        raise ValueError("block_q and block_k must be >= 1")
+    _check_lists(kv_idx, kv_cnt, (mask_heads, -(-n // block_q)), q8.device)
+    if block_valid is not None:
+        _expect(block_valid, "block_valid", dtype=torch.int32, device=q8.device, min_numel=-(-n // block_k))
     if out is None:
         out = torch.empty((heads, n, d), dtype=torch.float32, device=q8.device)
     _contig_cuda(q8, k8, vt8, q_scale, k_scale, v_scale, out, kv_idx, kv_cnt, block_valid)
@@ -334,7 +452,10 @@ def draft_attn_fwd_fp8(q8, k8, vt8, q_scale, k_scale, v_scale, T: int, H: int, g
     """FP8 Draft attention on the raster layout: codes of q, k [heads, T*H*grid_w, 128] and
     vt8 [heads, 128, ldv], per-head lists kv_idx [heads, nb, k], kv_cnt [heads, nb]; returns O fp32."""
     torch = _torch()
+    _check_fp8(q8, k8, vt8, q_scale, k_scale, v_scale, out)
     heads, n, d = q8.shape
+    nb = _draft_blocks(n, T, H, grid_w, pool_h, pool_w)
+    _check_lists(kv_idx, kv_cnt, (heads, nb), q8.device)
     if out is None:
         out = torch.empty((heads, n, d), dtype=torch.float32, device=q8.device)
     _contig_cuda(q8, k8, vt8, q_scale, k_scale, v_scale, out, kv_idx, kv_cnt)
@@ -348,6 +469,7 @@ def draft_attn_fwd_fp8(q8, k8, vt8, q_scale, k_scale, v_scale, T: int, H: int, g
 def dense_attn_fwd_fp8(q8, k8, vt8, q_scale, k_scale, v_scale, scale: float | None = None, out=None, stream=None):
     """Dense attention on E4M3 codes; returns O fp32 [heads, n, 128]."""
     torch = _torch()
+    _check_fp8(q8, k8, vt8, q_scale, k_scale, v_scale, out)
     heads, n, d = q8.shape
     if out is None:
         out = torch.empty((heads, n, d), dtype=torch.float32, device=q8.device)
