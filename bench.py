@@ -1,9 +1,10 @@
 #!/usr/bin/env python3
 """Benchmark of the block-sparse video-DiT attention path on one MI355X.
 
-Default workload: Wan-2.1-1.3B-shaped attention at 6x training length
-(T = 126 latent frames of 30x52 tokens, N = 196560, 12 heads, d = 128, bf16)
-with the LVSA frame mask (C = 21, W = 5, T_per = 8). One step = one pass of
+Default workload: Wan-2.1-14B-shaped single-layer attention at 6x training
+length (T = 126 latent frames of 30x52 tokens, N = 196560, 40 heads,
+d = 128, bf16) with the LVSA frame mask (C = 21, W = 5, T_per = 8): the
+largest of the workloads that fits one GPU. One step = one pass of
 the path: build the LVSA mask for denoising step s (s advances every step)
 and run the block-sparse attention over it. Inputs are seeded synthetic
 tensors with the workload's shapes, resident in HBM before timing starts.
@@ -68,17 +69,26 @@ def lvsa_pairs(w, kv_cnt_host) -> int:
     return int(w.heads) * w.P * w.P * int(kv_cnt_host.sum())
 
 
-def traffic_for(workload: str, kernel_src: str):
-    """HBM bytes per launch from the committed rocprofv3 --pmc summary, if it
-    was taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+def _record(kind: str, workload: str, kernel_src: str):
+    """A committed rocprofv3 summary (profiles/<kind>_<workload>.json) and a note
+    of where it came from, if it was taken on the current kernel code; else
+    (None, None). Its figures come from separate profiled runs, not this one."""
+    rel = os.path.join("profiles", f"{kind}_{workload}.json")
+    path = os.path.join(ROOT, rel)
     if not os.path.exists(path):
-        return None
+        return None, None
     with open(path) as f:
         t = json.load(f)
     if t.get("kernel_code_sha256_16") != src_hash(kernel_src):
-        return None
-    return t.get("hbm_bytes_per_launch")
+        return None, None
+    return t, {"file": rel, "kernel_code_sha256_16": t["kernel_code_sha256_16"],
+               "measured": "separate rocprofv3 runs of the commands in the file, not this run"}
+
+
+def traffic_for(workload: str, kernel_src: str):
+    """(HBM bytes per launch, source) from the committed rocprofv3 --pmc summary."""
+    t, src = _record("traffic", workload, kernel_src)
+    return (None, None) if t is None else (t.get("hbm_bytes_per_launch"), src)
 
 
 def oracle_threads() -> int:
@@ -92,16 +102,12 @@ def oracle_threads() -> int:
 
 
 def counters_for(workload: str, kernel_src: str):
-    """Counter evidence (clock, MFMA busy, L2 hit) from the committed rocprofv3
-    summary, if it was taken on the current kernel code; else None."""
-    path = os.path.join(ROOT, "profiles", f"counters_{workload}.json")
-    if not os.path.exists(path):
+    """(counter figures, source): clock, MFMA busy, L2 hit from the committed
+    rocprofv3 summary, if it was taken on the current kernel code."""
+    t, src = _record("counters", workload, kernel_src)
+    if t is None:
         return None
-    with open(path) as f:
-        t = json.load(f)
-    if t.get("kernel_code_sha256_16") != src_hash(kernel_src):
-        return None
-    return t.get("metrics")
+    return dict(t.get("metrics", {}), source=src)
 
 
 def median(xs):
@@ -332,17 +338,20 @@ def run_lvsa(args, w):
     if fp8:
         res["quantize_ms"] = round(quant_ms, 4)
         res["pct_fp8_peak"] = round(100.0 * achieved / PEAK_FP8_TFLOPS, 2)
+    # the counter records were taken at the workload's own frame budget
+    traffic, tsrc = traffic_for(w.name + ("-fp8" if fp8 else ""), ATTN_FP8_SRC if fp8 else ATTN_SRC) \
+        if own_budget else (None, None)
     res["roofline"] = {
         "bound": "mfma",
         "achieved": round(achieved, 2),
         "peak": peak,
         "unit": "TFLOP/s",
         "frac": round(achieved / peak, 4),
-        # the counter records were taken at the workload's own frame budget
-        "traffic": traffic_for(w.name + ("-fp8" if fp8 else ""), ATTN_FP8_SRC if fp8 else ATTN_SRC)
-        if own_budget else None,
+        "traffic": traffic,
         "kernel": "bsa_fwd_fp8_kernel<MODE_LIST, 4>" if fp8 else "bsa_fwd_d128_kernel<MODE_LIST, false>",
     }
+    if tsrc is not None:
+        res["roofline"]["traffic_source"] = tsrc
     ctr = counters_for(w.name + ("-fp8" if fp8 else ""), ATTN_FP8_SRC if fp8 else ATTN_SRC) if own_budget else None
     if ctr is not None:
         res["counters"] = ctr
@@ -497,15 +506,18 @@ def run_draft(args, w):
         "roofline": {"bound": "mfma", "achieved": round(flops / (attn_avg * 1e-3) / 1e12, 2),
                      "peak": PEAK_FP8_TFLOPS if fp8 else PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(flops / (attn_avg * 1e-3) / 1e12 / (PEAK_FP8_TFLOPS if fp8 else PEAK_BF16_TFLOPS), 4),
-                     # the counter records were taken on the reorder path at the workload's own
-                     # sparsity with mean pooling; other settings move other bytes
-                     "traffic": (None if not (reorder and sparsity == w.sparsity and pool == "mean") else
-                                 traffic_for(w.name + "-fp8", ATTN_FP8_SRC) if fp8 else traffic_for(w.name, ATTN_SRC)),
+                     "traffic": None,
                      "kernel": ("bsa_fwd_fp8_kernel<MODE_LIST, 4>" if reorder else "bsa_fwd_fp8_kernel<MODE_T2D, 4>")
                      if fp8 else ("bsa_fwd_d128_kernel<MODE_LIST, true>" if reorder
                                   else "bsa_fwd_d128_kernel<MODE_T2D, false>")},
     }
+    # the counter records were taken on the reorder path at the workload's own
+    # sparsity with mean pooling; other settings move other bytes
     if reorder and sparsity == w.sparsity and pool == "mean":
+        traffic, tsrc = traffic_for(w.name + ("-fp8" if fp8 else ""), ATTN_FP8_SRC if fp8 else ATTN_SRC)
+        res["roofline"]["traffic"] = traffic
+        if tsrc is not None:
+            res["roofline"]["traffic_source"] = tsrc
         ctr = counters_for(w.name + ("-fp8" if fp8 else ""), ATTN_FP8_SRC if fp8 else ATTN_SRC)
         if ctr is not None:
             res["counters"] = ctr
@@ -601,7 +613,7 @@ def _profiled_kernel(workload: str, fp8: bool):
 def summarize(argv) -> int:
     sp = argparse.ArgumentParser(prog="bench.py --summarize")
     sp.add_argument("what", choices=("traffic", "counters", "trace"))
-    sp.add_argument("--workload", default="wan1.3b-6x")
+    sp.add_argument("--workload", default="wan14b-6x")
     sp.add_argument("--fp8", action="store_true")
     sp.add_argument("--fetch")
     sp.add_argument("--write")
@@ -715,7 +727,7 @@ def main(argv=None) -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=16)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="wan1.3b-6x", choices=sorted(WORKLOAD_NAMES))
+    ap.add_argument("--workload", default="wan14b-6x", choices=sorted(WORKLOAD_NAMES))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-dense", action="store_true")

@@ -101,7 +101,27 @@ def test_code_hash_ignores_comments_and_whitespace(tmp_path):
     assert bench.src_hash(str(a)) == bench.src_hash(str(b)) != bench.src_hash(str(c))
 
 
-@pytest.mark.parametrize("key", ["wan1.3b-6x", "wan1.3b-6x-fp8", "hunyuan-draft", "hunyuan-draft-fp8"])
+def test_records_carry_their_source(tmp_path, monkeypatch):
+    """Figures taken from a committed record name the file and the code hash,
+    and a record taken on other kernel code is not used."""
+    src = tmp_path / "k.hip"
+    src.write_text("int k() { return 1; }\n")
+    (tmp_path / "profiles").mkdir()
+    rec = {"kernel_code_sha256_16": bench.src_hash(str(src)), "hbm_bytes_per_launch": 123.0,
+           "metrics": {"l2_hit_rate": 0.5}, "commands": ["python3 bench.py"]}
+    for kind in ("traffic", "counters"):
+        (tmp_path / "profiles" / f"{kind}_w.json").write_text(json.dumps(rec))
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    val, where = bench.traffic_for("w", str(src))
+    assert val == 123.0 and where["file"] == os.path.join("profiles", "traffic_w.json")
+    assert where["kernel_code_sha256_16"] == rec["kernel_code_sha256_16"] and "not this run" in where["measured"]
+    ctr = bench.counters_for("w", str(src))
+    assert ctr["l2_hit_rate"] == 0.5 and ctr["source"]["file"].endswith("counters_w.json")
+    src.write_text("int k() { return 2; }\n")
+    assert bench.traffic_for("w", str(src)) == (None, None) and bench.counters_for("w", str(src)) is None
+
+
+@pytest.mark.parametrize("key", ["wan14b-6x", "wan1.3b-6x", "wan1.3b-6x-fp8", "hunyuan-draft", "hunyuan-draft-fp8"])
 def test_committed_records_name_their_commands(key):
     for kind in ("traffic", "counters"):
         path = os.path.join(ROOT, "profiles", f"{kind}_{key}.json")

@@ -374,7 +374,9 @@ def test_full_hunyuan_draft():
 
 
 def test_full_hunyuan_draft_raster():
-    """Full HunyuanVideo size: the raster path equals the reorder path bit for bit."""
+    """Full HunyuanVideo size: the raster path equals the reorder path bit for
+    bit, and its sampled rows of three heads match the oracle run on the
+    oracle's own Draft mask (which the GPU's lists must equal)."""
     torch = _torch()
     w, q, k, v = _full_inputs("hunyuan-draft")
     note("hunyuan draft raster vs reorder, full size")
@@ -384,7 +386,33 @@ def test_full_hunyuan_draft_raster():
                              out["kv_cnt"])
     torch.cuda.synchronize()
     assert torch.equal(o, o2)
+    heads = [2, 12, 22]
+    g = oracle.draft_grid(w.T, w.H, w.W, w.pool_h, w.pool_w)
+    kv, cnt, *_ = oracle.draft_mask(synth.bf16_to_f32(q[heads]), synth.bf16_to_f32(k[heads]), g, w.sparsity)
+    assert np.array_equal(to_host(out["kv_idx"])[heads], kv) and np.array_equal(to_host(out["kv_cnt"])[heads], cnt)
+    perm, inv, bv = oracle.draft_permutation(g)
+    rows = sample_frame_rows(np.random.default_rng(310), w.T, w.P, nframes=5, per_frame=48)
+    ref = oracle.draft_attention_original_order(q[heads], k[heads], v[heads], perm, inv, bv, g.block_size, kv, cnt,
+                                                rows=rows)
+    assert_attn_close(to_host(o2[heads])[:, rows], ref, what="hunyuan draft raster")
     del out, o, o2
+    torch.cuda.empty_cache()
+
+
+def test_full_hunyuan_dense():
+    """Dense attention at the HunyuanVideo Draft shape (33 x 45 x 80 = 118800
+    tokens, 24 heads), the baseline the Draft speedup is quoted against:
+    sampled rows of three heads, including the ragged end of the sequence."""
+    torch = _torch()
+    w, q, k, v = _full_inputs("hunyuan-draft")
+    note("hunyuan dense, full shape")
+    o = _lib.dense_attn_fwd(to_dev(q), to_dev(k), to_dev(v))
+    heads = [1, 10, 23]
+    rows = sample_frame_rows(np.random.default_rng(320), w.T, w.P, nframes=4, per_frame=24)
+    got = to_host(o[heads])[:, rows]
+    ref = oracle.dense_attention(q, k, v, rows=rows, heads=heads)
+    assert_attn_close(got, ref, what="hunyuan dense")
+    del o
     torch.cuda.empty_cache()
 
 

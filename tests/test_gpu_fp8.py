@@ -527,12 +527,15 @@ def test_full_hunyuan_draft_fp8():
     deq = [oracle.dequantize(*oracle.quantize_per_head(synth.bf16_to_f32(x[heads]))) for x in (q, k, v)]
     g = oracle.draft_grid(w.T, w.H, w.W, w.pool_h, w.pool_w)
     perm, inv, bv = oracle.draft_permutation(g)
-    kv, cnt = to_host(out["kv_idx"])[heads], to_host(out["kv_cnt"])[heads]
+    # the oracle's own mask for these heads (the GPU's lists must equal it)
+    kv, cnt, *_ = oracle.draft_mask(synth.bf16_to_f32(q[heads]), synth.bf16_to_f32(k[heads]), g, w.sparsity)
+    assert np.array_equal(to_host(out["kv_idx"])[heads], kv) and np.array_equal(to_host(out["kv_cnt"])[heads], cnt)
     rows = sample_frame_rows(np.random.default_rng(800), w.T, w.P, nframes=4, per_frame=48)
     ref, bound, model, slack = (
         oracle.draft_attention_original_order(*deq, perm, inv, bv, g.block_size, kv, cnt, rows=rows, fn=f)
         for f in (None, oracle.p_rounding_bound, oracle.attention_p_e4m3, _acc_slack))
-    got = to_host(o)[heads][:, rows]
-    _assert_within_bound(got, ref, bound, model, float(np.abs(deq[2]).max()), "hunyuan draft fp8", slack)
+    for what, res in (("reorder", o), ("raster", o2)):
+        got = to_host(res[heads])[:, rows]
+        _assert_within_bound(got, ref, bound, model, float(np.abs(deq[2]).max()), f"hunyuan draft fp8 {what}", slack)
     del o, o2, out
     torch.cuda.empty_cache()
