@@ -59,6 +59,12 @@ def load() -> ctypes.CDLL:
         path = os.environ.get("LVSA_LIBRARY", LIB_PATH)
         if not os.path.exists(path):
             raise ImportError(f"{path} is missing: build it with `python -m video_diffusion_transformer_lvsa_amd.build`")
+        # torch ships its own HIP runtime. Loading it first makes the library
+        # bind to that same runtime (one device context; torch's streams and
+        # pointers are valid in the library). Opened first, the library would
+        # pull in the system runtime and torch would then load a second one,
+        # which finds no device.
+        _torch()
         lib = ctypes.CDLL(path)
         for name, (res, args) in SIGNATURES.items():
             f = getattr(lib, name)

@@ -39,9 +39,10 @@ int g_dev_ok[64];  // 0 unknown, 1 ok, -1 bad
 
 int check_device() {
   int n = 0;
-  if (hipGetDeviceCount(&n) != hipSuccess || n <= 0) {
+  const hipError_t ec = hipGetDeviceCount(&n);
+  if (ec != hipSuccess || n <= 0) {
     (void)hipGetLastError();
-    return fail(LVSA_EDEVICE, "no GPU visible to HIP");
+    return fail(LVSA_EDEVICE, "no GPU visible to HIP (%s, %d devices)", hipGetErrorString(ec), n);
   }
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) {
