@@ -145,6 +145,27 @@ int draft_mask_and_perm(const void* q, const void* k, const void* v, int dt, int
                         int32_t* perm, int32_t* inv_perm, int32_t* block_valid, void* q_perm, void* k_perm,
                         void* v_perm, void* workspace, size_t ws_bytes, void* stream);
 
+/* draft_mask_and_perm for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments and outputs without the workspace, which
+ * comes from a device array the library holds, one copy per GPU, reserved
+ * when the library is loaded and kept until the process ends. The call makes
+ * no hipMalloc, hipFree or other allocation; the caller still passes every
+ * input and output buffer.
+ *   Limit: 3*heads*nb*d*4 bytes (pooled Q̄, K̄ and K̄ᵀ) must fit in
+ *   LVSA_NOALLOC_SCRATCH_BYTES, i.e. heads*nb*d <= 4194304 (the
+ *   HunyuanVideo-shaped 24 heads x 990 blocks x 128 channels needs
+ *   3041280); larger requests return LVSA_ENOMEM before anything runs.
+ *   Every call on one GPU uses that GPU's one array, and each call writes
+ *   all of the part it reads, so nothing is carried from the previous call;
+ *   calls that overlap in time on the same GPU (other streams, other host
+ *   threads) race on it and must be serialised by the caller. */
+#define LVSA_NOALLOC_SCRATCH_BYTES ((size_t)48 << 20)
+int draft_mask_and_perm_noalloc(const void* q, const void* k, const void* v, int dt, int heads, int T, int H,
+                                int grid_w, int d, int pool_h, int pool_w, double sparsity, int pool_mode,
+                                int32_t* kv_idx, int32_t* kv_cnt, int32_t* perm, int32_t* inv_perm,
+                                int32_t* block_valid, void* q_perm, void* k_perm, void* v_perm, void* stream);
+
 /* The draft map itself, materialised: scores [heads, nb_q, nb_k] fp32 from
  * q̄ [heads, nb_q, d] and k̄ [heads, nb_k, d] fp32, same fixed arithmetic as
  * above. For inspection and testing; draft_mask_and_perm never stores it. */

@@ -30,6 +30,7 @@ SIGNATURES = {
     "draft_grid_info": (_c_int, [_c_int] * 5 + [_c_dbl, _pint, _pint, _pint, _pint]),
     "draft_workspace_bytes": (_c_sz, [_c_int] * 7),
     "draft_mask_and_perm": (_c_int, [_p, _p, _p] + [_c_int] * 8 + [_c_dbl, _c_int] + [_p] * 9 + [_c_sz, _p]),
+    "draft_mask_and_perm_noalloc": (_c_int, [_p, _p, _p] + [_c_int] * 8 + [_c_dbl, _c_int] + [_p] * 8 + [_p]),
     "draft_scores": (_c_int, [_p, _p] + [_c_int] * 4 + [_p, _p]),
     "token_permute": (_c_int, [_p, _p] + [_c_int] * 5 + [_p, _p]),
     "block_sparse_attn_fwd": (_c_int, [_p] * 4 + [_c_int] * 6 + [_p, _p, _c_int, _c_int, _p, _c_flt, _p]),
@@ -270,6 +271,42 @@ def draft_mask_and_perm(q, k, v, T: int, H: int, grid_w: int, pool_h: int, pool_
         _stream(stream)))
     out["qbar"] = ws[: heads * nb * d].view(heads, nb, d)
     out["kbar"] = ws[heads * nb * d : 2 * heads * nb * d].view(heads, nb, d)
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 48 << 20  # LVSA_NOALLOC_SCRATCH_BYTES
+
+
+def draft_mask_and_perm_noalloc(q, k, v, T: int, H: int, grid_w: int, pool_h: int, pool_w: int, sparsity: float,
+                                out: dict, pool: str = "mean", stream=None) -> dict:
+    """draft_mask_and_perm without a workspace: the library's own device
+    scratch holds the pooled Q and K, so nothing is allocated, here or in the
+    library. `out` must hold every output, preallocated: kv_idx, kv_cnt,
+    perm, inv_perm, block_valid and, to reorder, q_perm, k_perm, v_perm (all
+    three, or none of them)."""
+    torch = _torch()
+    _check_qkv(q, k, v)
+    heads, n, d = q.shape
+    if n != T * H * grid_w:
+        raise ValueError(f"q has {n} tokens; the grid {T}x{H}x{grid_w} has {T * H * grid_w}")
+    if pool not in POOL_MODES:
+        raise ValueError(f"pool must be one of {sorted(POOL_MODES)}")
+    info = draft_grid_info(T, H, grid_w, pool_h, pool_w, sparsity)
+    nb, n_pad, topk = info["nb"], info["n_pad"], info["k"]
+    want = {"kv_idx": ((heads, nb, topk), torch.int32), "kv_cnt": ((heads, nb), torch.int32),
+            "perm": ((n_pad,), torch.int32), "inv_perm": ((n,), torch.int32), "block_valid": ((nb,), torch.int32)}
+    perm_names = [x for x in ("q_perm", "k_perm", "v_perm") if out.get(x) is not None]
+    if perm_names and len(perm_names) != 3:
+        raise ValueError("q_perm, k_perm, v_perm: give all three or none")
+    for name in perm_names:
+        want[name] = ((heads, n_pad, d), q.dtype)
+    for name, (shape, dt) in want.items():
+        _expect(out.get(name), name, shape, dt, q.device)
+    _contig_cuda(q, k, v, *(out[x] for x in want))
+    _check(load().draft_mask_and_perm_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _dt(q), heads, T, H, grid_w, d, pool_h, pool_w, sparsity, POOL_MODES[pool],
+        _ptr(out["kv_idx"]), _ptr(out["kv_cnt"]), _ptr(out["perm"]), _ptr(out["inv_perm"]), _ptr(out["block_valid"]),
+        _ptr(out.get("q_perm")), _ptr(out.get("k_perm")), _ptr(out.get("v_perm")), _stream(stream)))
     return out
 
 

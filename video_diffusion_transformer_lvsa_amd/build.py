@@ -30,6 +30,7 @@ SOURCES = {
     "draft.hip": ["-ffp-contract=off"],
     "fp8.hip": [],
     "attn_fp8.hip": [],
+    "scratch.hip": [],
 }
 
 COMMON = [

@@ -254,11 +254,14 @@ size_t draft_workspace_bytes(int heads, int T, int H, int grid_w, int d, int poo
   return 3 * (size_t)heads * g.nb * d * sizeof(float);
 }
 
-int draft_mask_and_perm(const void* q, const void* k, const void* v, int dt, int heads, int T, int H, int grid_w,
-                        int d, int pool_h, int pool_w, double sparsity, int pool_mode, int32_t* kv_idx, int32_t* kv_cnt,
-                        int32_t* perm, int32_t* inv_perm, int32_t* block_valid, void* q_perm, void* k_perm,
-                        void* v_perm, void* workspace, size_t ws_bytes, void* stream) {
-  clear_err();
+namespace {
+
+// Shared by draft_mask_and_perm and its no-allocation variant: validation and
+// the three launches. workspace == NULL means "use the library's scratch".
+int draft_mask_impl(const void* q, const void* k, const void* v, int dt, int heads, int T, int H, int grid_w, int d,
+                    int pool_h, int pool_w, double sparsity, int pool_mode, int32_t* kv_idx, int32_t* kv_cnt,
+                    int32_t* perm, int32_t* inv_perm, int32_t* block_valid, void* q_perm, void* k_perm, void* v_perm,
+                    void* workspace, size_t ws_bytes, bool own_scratch, void* stream) {
   if (dt != LVSA_F32 && dt != LVSA_BF16) return fail(LVSA_EINVAL, "dtype %d unknown", dt);
   if (d != 64 && d != 128) return fail(LVSA_EUNSUPPORTED, "head dim d=%d (supported: 64, 128)", d);
   if (heads < 1) return fail(LVSA_EINVAL, "heads=%d must be >= 1", heads);
@@ -281,9 +284,19 @@ int draft_mask_and_perm(const void* q, const void* k, const void* v, int dt, int
       !aligned16(v_perm) || !aligned16(workspace))
     return fail(LVSA_EINVAL, "tensors and workspace must be 16-byte aligned");
   const size_t need = 3 * (size_t)heads * g.nb * d * sizeof(float);
-  if (!workspace || ws_bytes < need) return fail(LVSA_ENOMEM, "workspace %zu bytes < required %zu", ws_bytes, need);
+  if (own_scratch) {
+    if (need > lvsa::kScratchBytes)
+      return fail(LVSA_ENOMEM, "pooled Q, K need %zu bytes of scratch; the library holds %zu (heads*nb*d <= %zu)", need,
+                  lvsa::kScratchBytes, lvsa::kScratchBytes / (3 * sizeof(float)));
+  } else if (!workspace || ws_bytes < need) {
+    return fail(LVSA_ENOMEM, "workspace %zu bytes < required %zu", ws_bytes, need);
+  }
   rc = check_device();
   if (rc) return rc;
+  if (own_scratch) {
+    rc = launched(lvsa::scratch_address(&workspace), "scratch address lookup");
+    if (rc) return rc;
+  }
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   float* qbar = static_cast<float*>(workspace);
   float* kbar = qbar + (size_t)heads * g.nb * d;
@@ -296,6 +309,26 @@ int draft_mask_and_perm(const void* q, const void* k, const void* v, int dt, int
   if (rc) return rc;
   return launched(lvsa::launch_draft_select(qbar, kbarT, heads, g.nb, d, topk, kv_idx, kv_cnt, s),
                   "draft select launch");
+}
+
+}  // namespace
+
+int draft_mask_and_perm(const void* q, const void* k, const void* v, int dt, int heads, int T, int H, int grid_w,
+                        int d, int pool_h, int pool_w, double sparsity, int pool_mode, int32_t* kv_idx, int32_t* kv_cnt,
+                        int32_t* perm, int32_t* inv_perm, int32_t* block_valid, void* q_perm, void* k_perm,
+                        void* v_perm, void* workspace, size_t ws_bytes, void* stream) {
+  clear_err();
+  return draft_mask_impl(q, k, v, dt, heads, T, H, grid_w, d, pool_h, pool_w, sparsity, pool_mode, kv_idx, kv_cnt,
+                         perm, inv_perm, block_valid, q_perm, k_perm, v_perm, workspace, ws_bytes, false, stream);
+}
+
+int draft_mask_and_perm_noalloc(const void* q, const void* k, const void* v, int dt, int heads, int T, int H,
+                                int grid_w, int d, int pool_h, int pool_w, double sparsity, int pool_mode,
+                                int32_t* kv_idx, int32_t* kv_cnt, int32_t* perm, int32_t* inv_perm,
+                                int32_t* block_valid, void* q_perm, void* k_perm, void* v_perm, void* stream) {
+  clear_err();
+  return draft_mask_impl(q, k, v, dt, heads, T, H, grid_w, d, pool_h, pool_w, sparsity, pool_mode, kv_idx, kv_cnt,
+                         perm, inv_perm, block_valid, q_perm, k_perm, v_perm, nullptr, 0, true, stream);
 }
 
 int draft_scores(const float* qbar, const float* kbar, int heads, int nb_q, int nb_k, int d, float* scores,

@@ -86,6 +86,12 @@ hipError_t launch_draft_scores(const float* qbar, const float* kbar, int heads, 
 // 16, >= n); scales[h] receives the dequantization factor.
 hipError_t launch_quantize_fp8(const void* src, int dt, int heads, int n, int d, bool transpose, int ld,
                                uint8_t* dst, float* scales, hipStream_t s);
+// Size of the library-owned device scratch (one copy per GPU, held until the
+// process ends) that draft_mask_and_perm_noalloc uses as its workspace.
+constexpr size_t kScratchBytes = (size_t)48 << 20;
+// Address of the current device's scratch (looked up once per device).
+hipError_t scratch_address(void** out);
+
 hipError_t launch_token_permute(const void* src, void* dst, int esize, int heads, int n_src, int n_dst, int d,
                                 const int32_t* map, hipStream_t s);
 
