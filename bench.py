@@ -508,17 +508,18 @@ def run_draft(args, w):
                      "frac": round(flops / (attn_avg * 1e-3) / 1e12 / (PEAK_FP8_TFLOPS if fp8 else PEAK_BF16_TFLOPS), 4),
                      "traffic": None,
                      "kernel": ("bsa_fwd_fp8_kernel<MODE_LIST, 4>" if reorder else "bsa_fwd_fp8_kernel<MODE_T2D, 4>")
-                     if fp8 else ("bsa_fwd_d128_kernel<MODE_LIST, true>" if reorder
-                                  else "bsa_fwd_d128_kernel<MODE_T2D, false>")},
+                     if fp8 else ("bsa_fwd_d128_kernel<MODE_GRP, true>" if reorder
+                                  else "bsa_fwd_d128_kernel<MODE_T2DG, false>")},
     }
-    # the counter records were taken on the reorder path at the workload's own
-    # sparsity with mean pooling; other settings move other bytes
-    if reorder and sparsity == w.sparsity and pool == "mean":
-        traffic, tsrc = traffic_for(w.name + ("-fp8" if fp8 else ""), ATTN_FP8_SRC if fp8 else ATTN_SRC)
+    # the counter records were taken at the workload's own sparsity with mean
+    # pooling, one record per path; other settings move other bytes
+    if sparsity == w.sparsity and pool == "mean":
+        key = w.name + ("" if reorder else "-raster") + ("-fp8" if fp8 else "")
+        traffic, tsrc = traffic_for(key, ATTN_FP8_SRC if fp8 else ATTN_SRC)
         res["roofline"]["traffic"] = traffic
         if tsrc is not None:
             res["roofline"]["traffic_source"] = tsrc
-        ctr = counters_for(w.name + ("-fp8" if fp8 else ""), ATTN_FP8_SRC if fp8 else ATTN_SRC)
+        ctr = counters_for(key, ATTN_FP8_SRC if fp8 else ATTN_SRC)
         if ctr is not None:
             res["counters"] = ctr
     if not args.no_dense:
@@ -591,23 +592,28 @@ def _per_kernel(rows, counter: str):
     return out
 
 
-def _profiled_kernel(workload: str, fp8: bool):
+def _profiled_kernel(workload: str, fp8: bool, raster: bool = False):
     """(source, kernel key in traces, label, traffic/counter key, algorithmic bytes per launch)."""
     from video_diffusion_transformer_lvsa_amd import synth
 
     w = synth.WORKLOADS[workload]
-    if w.kind == "draft":
+    if w.kind == "draft" and not raster:
         nb = w.T * (-(-w.H // w.pool_h)) * (-(-w.W // w.pool_w))
         n = nb * w.pool_h * w.pool_w
     else:
         n = w.N
     elem = 1 if fp8 else 2
     alg = 3 * w.heads * n * w.d * elem + w.heads * n * w.d * 4
+    key = w.name + ("-raster" if raster else "") + ("-fp8" if fp8 else "")
     if fp8:
-        return ATTN_FP8_SRC, "bsa_fwd_fp8_kernel<1, 4>", "bsa_fwd_fp8_kernel<MODE_LIST, 4>", w.name + "-fp8", alg
-    tmpl = "bsa_fwd_d128_kernel<1, true>" if w.kind == "draft" else "bsa_fwd_d128_kernel<1, false>"
-    label = "bsa_fwd_d128_kernel<MODE_LIST, true>" if w.kind == "draft" else "bsa_fwd_d128_kernel<MODE_LIST, false>"
-    return ATTN_SRC, tmpl, label, w.name, alg
+        mode = ("3", "MODE_T2D") if raster else ("1", "MODE_LIST")
+        return ATTN_FP8_SRC, f"bsa_fwd_fp8_kernel<{mode[0]}, 4>", f"bsa_fwd_fp8_kernel<{mode[1]}, 4>", key, alg
+    if w.kind == "draft":
+        tmpl, label = (("bsa_fwd_d128_kernel<5, false>", "bsa_fwd_d128_kernel<MODE_T2DG, false>") if raster else
+                       ("bsa_fwd_d128_kernel<4, true>", "bsa_fwd_d128_kernel<MODE_GRP, true>"))
+    else:
+        tmpl, label = "bsa_fwd_d128_kernel<1, false>", "bsa_fwd_d128_kernel<MODE_LIST, false>"
+    return ATTN_SRC, tmpl, label, key, alg
 
 
 def summarize(argv) -> int:
@@ -615,6 +621,7 @@ def summarize(argv) -> int:
     sp.add_argument("what", choices=("traffic", "counters", "trace"))
     sp.add_argument("--workload", default="wan14b-6x")
     sp.add_argument("--fp8", action="store_true")
+    sp.add_argument("--no-reorder", action="store_true", help="Draft: records of the raster path")
     sp.add_argument("--fetch")
     sp.add_argument("--write")
     sp.add_argument("--calib-copy-mb", type=int, default=1024)
@@ -637,7 +644,7 @@ def summarize(argv) -> int:
         with open(a.out, "w") as f:
             f.write("\n".join(lines) + "\n")
         return 0
-    src, key, label, tkey, alg = _profiled_kernel(a.workload, a.fp8)
+    src, key, label, tkey, alg = _profiled_kernel(a.workload, a.fp8, a.no_reorder)
     if a.what == "traffic":
         fr, wr = _per_kernel(_csv_in(a.fetch, "counter_collection.csv"), "FETCH_SIZE"), \
             _per_kernel(_csv_in(a.write, "counter_collection.csv"), "WRITE_SIZE")
@@ -649,7 +656,8 @@ def summarize(argv) -> int:
         cw = sum(wr[cal][:3]) / 3
         ff, fw = known_r / cf, known_w / cw
         mean = lambda v: sum(v) / len(v)
-        t = {"kernel": label, "workload": WORKLOAD_NAMES[a.workload] + ("-fp8" if a.fp8 else ""),
+        t = {"kernel": label, "workload": WORKLOAD_NAMES[a.workload] + ("-raster" if a.no_reorder else "")
+             + ("-fp8" if a.fp8 else ""),
              "kernel_code_sha256_16": src_hash(src),
              "fetch_size_kib_raw": mean(fr[key]), "write_size_kib_raw": mean(wr[key]),
              "copy_calibration": {"kernel": f"token_permute_kernel (identity map, {a.calib_copy_mb} MiB)",
@@ -701,7 +709,8 @@ def summarize(argv) -> int:
             met["lds_bank_conflicts"] = m["SQ_LDS_BANK_CONFLICT"]
         if "SQ_INSTS_LDS" in m:
             met["lds_insts_per_launch"] = m["SQ_INSTS_LDS"]
-        t = {"kernel": label, "workload": WORKLOAD_NAMES[a.workload] + ("-fp8" if a.fp8 else ""),
+        t = {"kernel": label, "workload": WORKLOAD_NAMES[a.workload] + ("-raster" if a.no_reorder else "")
+             + ("-fp8" if a.fp8 else ""),
              "kernel_code_sha256_16": src_hash(src), "metrics": met,
              "derivation": {"shader_clock_ghz": "GRBM_GUI_ACTIVE / 8 XCDs / dispatch duration",
                             "mfma_busy_frac": "SQ_VALU_MFMA_BUSY_CYCLES / 1024 SIMDs / (GRBM_GUI_ACTIVE / 8)",

@@ -21,7 +21,7 @@ constexpr float kRescale = 8.0f;            // log2 headroom before the referenc
 constexpr float kSumBf16 = 65536.0f;        // bf16 d = 128: largest lane sum of a tile's probabilities
 constexpr float kSumFp8 = 256.0f;           // FP8: the same, so that every probability is <= 2^8 < 448
 
-enum { MODE_DENSE = 0, MODE_LIST = 1, MODE_SMALL = 2, MODE_T2D = 3 };
+enum { MODE_DENSE = 0, MODE_LIST = 1, MODE_SMALL = 2, MODE_T2D = 3, MODE_GRP = 4, MODE_T2DG = 5 };
 
 // Where the BN virtual key rows of one tile live. Uniform across the workgroup.
 // Row r < bnd is physical row base0 + r, row r >= bnd is base1 + r; row r is
@@ -172,6 +172,101 @@ __device__ __forceinline__ TileD stream_tile(const TileStream& ts, const AttnArg
   } else {
     t.base0 = t.base1 = t.bnd = t.v0 = t.v1 = 0;
     t.full = 0;
+  }
+  return t;
+}
+
+// ---------------------------------------------------------------------------
+// Compacted key walk in 16-row groups (MODE_GRP: lists over blocks with
+// per-block valid counts; MODE_T2DG: raster pool tiles 16 tokens wide). A
+// listed block contributes its valid rows only, as groups of up to 16
+// consecutive physical rows: MODE_GRP rows 16g .. 16g+15 of the block (the
+// last group of a block may be short), MODE_T2DG pool row g (its valid
+// columns). A 64-key tile is four consecutive groups, so the empty part of a
+// partly valid block costs no tile. The order of the keys is the list order,
+// then the row order inside a block: the reordered and the raster layout of
+// the same pool tiles produce the same tiles.
+// ---------------------------------------------------------------------------
+struct GTile {
+  int base[4];  // first physical row of group j
+  int nv[4];    // valid rows of group j (0 .. 16)
+  int full;     // every group has 16 valid rows
+};
+
+struct GStream {
+  int slot;  // list slot of the next group
+  int g;     // next group inside that slot
+  int ng;    // groups of that slot (0: the list is exhausted)
+  int blk;   // its KV block
+  int lim;   // MODE_GRP: valid rows of the block; MODE_T2DG: valid columns
+  int tok;   // MODE_T2DG: first token of the block
+};
+
+// Groups of list slot `slot` (0 for an invalid entry or an empty block).
+template <int MODE>
+__device__ __forceinline__ int slot_groups(const AttnArgs& a, const int32_t* list, int cnt, int slot, int& blk,
+                                           int& lim, int& tok) {
+  blk = list_entry(a, list, cnt, slot);
+  tok = 0;
+  lim = 0;
+  if (blk < 0) return 0;
+  if (MODE == MODE_GRP) {
+    lim = block_lim(a, blk);
+    return (lim + 15) >> 4;
+  }
+  const BlkGeom geo = blk_geom(a, blk);
+  tok = geo.tok;
+  lim = geo.vw;
+  return geo.vw > 0 ? geo.vh : 0;
+}
+
+// Moves s to the first slot at or after s.slot that has groups.
+template <int MODE>
+__device__ __forceinline__ void gs_seek(GStream& s, const AttnArgs& a, const int32_t* list, int cnt) {
+  s.g = 0;
+  s.ng = 0;
+  while (s.slot < cnt) {
+    s.ng = slot_groups<MODE>(a, list, cnt, s.slot, s.blk, s.lim, s.tok);
+    if (s.ng > 0) return;
+    ++s.slot;
+  }
+}
+
+// Total groups of a list (the walk's length).
+template <int MODE>
+__device__ __forceinline__ int list_groups(const AttnArgs& a, const int32_t* list, int cnt) {
+  int total = 0;
+  for (int sl = 0; sl < cnt; ++sl) {
+    int blk, lim, tok;
+    total += slot_groups<MODE>(a, list, cnt, sl, blk, lim, tok);
+  }
+  return total;
+}
+
+// The next tile: four groups taken from s (empty groups past the end).
+template <int MODE>
+__device__ __forceinline__ GTile gs_tile(GStream& s, const AttnArgs& a, const int32_t* list, int cnt) {
+  GTile t;
+  t.full = 1;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if (s.ng == 0) {
+      t.base[j] = 0;
+      t.nv[j] = 0;
+    } else {
+      if (MODE == MODE_GRP) {
+        t.base[j] = s.blk * a.block_k + 16 * s.g;
+        t.nv[j] = min(16, s.lim - 16 * s.g);
+      } else {
+        t.base[j] = s.tok + s.g * a.gW;
+        t.nv[j] = min(16, s.lim);
+      }
+      if (++s.g == s.ng) {
+        ++s.slot;
+        gs_seek<MODE>(s, a, list, cnt);
+      }
+    }
+    t.full &= (t.nv[j] == 16);
   }
   return t;
 }
