@@ -37,6 +37,7 @@ PEAK_HBM_GBS = 8000.0
 METRIC = "block-sparse attn ms/call + effective TFLOP/s (% bf16 MFMA peak), 1 MI355X"
 ATTN_SRC = os.path.join(ROOT, "video_diffusion_transformer_lvsa_amd", "csrc", "attn_bf16.hip")
 ATTN_FP8_SRC = os.path.join(ROOT, "video_diffusion_transformer_lvsa_amd", "csrc", "attn_fp8.hip")
+ATTN_GRP_SRC = os.path.join(ROOT, "video_diffusion_transformer_lvsa_amd", "csrc", "attn_grp.hip")
 DRAFT_SRC = os.path.join(ROOT, "video_diffusion_transformer_lvsa_amd", "csrc", "draft.hip")
 
 WORKLOAD_NAMES = {
@@ -508,18 +509,18 @@ def run_draft(args, w):
                      "frac": round(flops / (attn_avg * 1e-3) / 1e12 / (PEAK_FP8_TFLOPS if fp8 else PEAK_BF16_TFLOPS), 4),
                      "traffic": None,
                      "kernel": ("bsa_fwd_fp8_kernel<MODE_LIST, 4>" if reorder else "bsa_fwd_fp8_kernel<MODE_T2D, 4>")
-                     if fp8 else ("bsa_fwd_d128_kernel<MODE_GRP, true>" if reorder
-                                  else "bsa_fwd_d128_kernel<MODE_T2DG, false>")},
+                     if fp8 else ("bsa_fwd_d128_grp_kernel<MODE_GRP, true>" if reorder
+                                  else "bsa_fwd_d128_grp_kernel<MODE_T2DG, false>")},
     }
     # the counter records were taken at the workload's own sparsity with mean
     # pooling, one record per path; other settings move other bytes
     if sparsity == w.sparsity and pool == "mean":
         key = w.name + ("" if reorder else "-raster") + ("-fp8" if fp8 else "")
-        traffic, tsrc = traffic_for(key, ATTN_FP8_SRC if fp8 else ATTN_SRC)
+        traffic, tsrc = traffic_for(key, ATTN_FP8_SRC if fp8 else ATTN_GRP_SRC)
         res["roofline"]["traffic"] = traffic
         if tsrc is not None:
             res["roofline"]["traffic_source"] = tsrc
-        ctr = counters_for(key, ATTN_FP8_SRC if fp8 else ATTN_SRC)
+        ctr = counters_for(key, ATTN_FP8_SRC if fp8 else ATTN_GRP_SRC)
         if ctr is not None:
             res["counters"] = ctr
     if not args.no_dense:
@@ -609,10 +610,10 @@ def _profiled_kernel(workload: str, fp8: bool, raster: bool = False):
         mode = ("3", "MODE_T2D") if raster else ("1", "MODE_LIST")
         return ATTN_FP8_SRC, f"bsa_fwd_fp8_kernel<{mode[0]}, 4>", f"bsa_fwd_fp8_kernel<{mode[1]}, 4>", key, alg
     if w.kind == "draft":
-        tmpl, label = (("bsa_fwd_d128_kernel<5, false>", "bsa_fwd_d128_kernel<MODE_T2DG, false>") if raster else
-                       ("bsa_fwd_d128_kernel<4, true>", "bsa_fwd_d128_kernel<MODE_GRP, true>"))
-    else:
-        tmpl, label = "bsa_fwd_d128_kernel<1, false>", "bsa_fwd_d128_kernel<MODE_LIST, false>"
+        tmpl, label = (("bsa_fwd_d128_grp_kernel<5, false>", "bsa_fwd_d128_grp_kernel<MODE_T2DG, false>") if raster
+                       else ("bsa_fwd_d128_grp_kernel<4, true>", "bsa_fwd_d128_grp_kernel<MODE_GRP, true>"))
+        return ATTN_GRP_SRC, tmpl, label, key, alg
+    tmpl, label = "bsa_fwd_d128_kernel<1, false>", "bsa_fwd_d128_kernel<MODE_LIST, false>"
     return ATTN_SRC, tmpl, label, key, alg
 
 

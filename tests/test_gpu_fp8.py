@@ -7,11 +7,12 @@
   mean of the dequantized V over each query's key set. With integer-valued V
   (scale 1) every partial sum is an exact integer, so this pins the key
   lists, the transposed V operand and its scale up to the final fp32
-  division. With random V it measures the FP8 matrix core's accumulation:
-  the hardware does not return the correctly rounded sum of a 64-product
-  block; on MI355X the sum of a block stays within 2^-13 of its largest
-  |term| (test_fp8_mfma_block_accumulation measures it directly and prints
-  the worst case), the slack every FP8 tolerance below adds.
+  division. With random V it measures the FP8 matrix core's accumulation,
+  which is not the correctly rounded sum when a 64-product block spans a
+  wide range of magnitudes: test_fp8_mfma_block_accumulation measures it
+  (2^-22 of the largest term over 8 octaves, 2^-11.3 over the whole E4M3
+  range); every FP8 tolerance below adds a slack of 2^-13 of the largest
+  term per tile, which covers the inputs of these cases.
 * Attention on random inputs, against the oracle's fp64 attention on the
   dequantized values: every element within the derived bound of
   oracle.p_rounding_bound (the only inexact step is the E4M3 rounding of the
@@ -126,7 +127,11 @@ def _run_fp8(dev, block_q=None, block_k=None, idx=None, cnt=None, mask_heads=1, 
     return _lib.block_sparse_attn_fwd_fp8(*args, block_q, block_k, idx, cnt, mask_heads=mask_heads, scale=scale)
 
 
-ACC_BLOCK = 2.0 ** -13  # FP8 MFMA: |block sum - exact| <= ACC_BLOCK * max |term| (64 products)
+# Slack per 64-key tile for the FP8 matrix core's accumulation, in units of the
+# largest |term|: frozen; test_fp8_mfma_block_accumulation measures what the
+# hardware does (inside it for products of similar size, up to 2^-11.3 for
+# blocks whose products span the whole E4M3 range).
+ACC_BLOCK = 2.0 ** -13
 
 
 def _assert_exact_mean(got, ref, what, vmax=None, l_min=64):
@@ -209,32 +214,44 @@ def test_fp8_dense_k_zero_is_mean_of_v(n):
 
 
 def test_fp8_mfma_block_accumulation():
-    """The measurement behind ACC_BLOCK. One 64-key tile with K = 0: every
-    probability is exactly 1, so each output element is the mean of 64 E4M3
-    V values, and 64 * O - sum_j v_j is the error of one 64-product block
-    sum of the FP8 matrix core (the factor 64 and the fp32 scalings are exact
-    or far below it). Random V with the full E4M3 range of magnitudes. The
-    test prints the largest error in units of the block's largest |term|
-    (log2) and holds it to ACC_BLOCK; the constant is frozen: a larger error
-    here is a finding about the kernel, not a reason to widen it."""
-    heads, n, d = 4, 64, 128
-    worst = 0.0
-    for seed in range(3):
-        rng = np.random.default_rng(900 + seed)
-        q = synth.bf16_round(rng.standard_normal((heads, n, d)).astype(np.float32))
-        k = np.zeros((heads, n, d), np.float32)
-        mag = np.exp2(rng.uniform(-8.0, 0.0, size=(heads, n, d)))
-        v = synth.bf16_round((rng.choice([-1.0, 1.0], size=(heads, n, d)) * mag * 448).astype(np.float32))
-        note(f"fp8 block accumulation seed={seed}")
-        dev, (_, _, dv) = _quant_pair(q, k, v)
-        got = to_host(_run_fp8(dev)).astype(np.float64)
-        exact = dv.sum(axis=1, keepdims=True)          # [heads, 1, d], exact in fp64
-        term = np.abs(dv).max(axis=1, keepdims=True)   # largest |term| of each block
-        err = np.abs(64.0 * got - exact) / term
-        worst = max(worst, float(err.max()))
-    note(f"fp8 block accumulation: largest error 2^{math.log2(worst) if worst > 0 else -math.inf:.2f} "
-         f"of the largest term (ACC_BLOCK = 2^{math.log2(ACC_BLOCK):.0f})")
-    assert worst <= ACC_BLOCK
+    """What the FP8 matrix core's accumulation does, measured. With K = 0
+    every probability is exactly 1, so n * O - sum_j v_j is the error of the
+    accumulation over the n keys (the scalings by 1/n and by the V scale are
+    exact or far below it). Three cases, each reported as the largest error
+    per 64-key tile in units of the largest |term| (log2):
+      * one tile, V over 8 octaves: the 64-product sum comes back correct to
+        fp32 rounding (measured 2^-22);
+      * one tile, V over the whole E4M3 range (subnormal codes included): the
+        matrix core loses the low bits of products far below the largest one
+        (measured 2^-11.3), more than ACC_BLOCK;
+      * 32 tiles over the whole range: the per-tile errors of the block sums
+        partly cancel in the fp32 accumulator (measured 2^-14.1).
+    ACC_BLOCK, the slack the parity tolerances add, covers the parity cases'
+    inputs (every one of them passes) but is not a bound for arbitrary
+    inputs; the limits below pin the measured behaviour, so a change of it
+    shows up here."""
+    heads, d = 4, 128
+    limits = {"one tile, 8 octaves": 2.0 ** -20, "one tile, full range": 2.0 ** -10,
+              "32 tiles, full range": 2.0 ** -12}
+    for name, n, octaves in (("one tile, 8 octaves", 64, 8.0), ("one tile, full range", 64, 18.0),
+                             ("32 tiles, full range", 2048, 18.0)):
+        worst = 0.0
+        for seed in range(3):
+            rng = np.random.default_rng(900 + 10 * n + seed + int(octaves))
+            q = synth.bf16_round(rng.standard_normal((heads, n, d)).astype(np.float32))
+            k = np.zeros((heads, n, d), np.float32)
+            mag = np.exp2(rng.uniform(-octaves, 0.0, size=(heads, n, d)))
+            v = synth.bf16_round((rng.choice([-1.0, 1.0], size=(heads, n, d)) * mag * 448).astype(np.float32))
+            note(f"fp8 accumulation, {name}, seed={seed}")
+            dev, (_, _, dv) = _quant_pair(q, k, v)
+            got = to_host(_run_fp8(dev)).astype(np.float64)
+            exact = dv.sum(axis=1, keepdims=True)          # [heads, 1, d], exact in fp64
+            term = np.abs(dv).max(axis=1, keepdims=True)   # largest |term| of the column
+            err = np.abs(n * got - exact) / (term * (n // 64))
+            worst = max(worst, float(err.max()))
+        note(f"fp8 accumulation, {name}: largest error per tile 2^{math.log2(worst) if worst > 0 else -math.inf:.2f} "
+             f"of the largest term (ACC_BLOCK = 2^{math.log2(ACC_BLOCK):.0f})")
+        assert worst <= limits[name], f"{name}: 2^{math.log2(worst):.2f}"
 
 
 LVSA_FP8 = [

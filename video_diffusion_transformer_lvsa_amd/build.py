@@ -25,6 +25,7 @@ ARCH = "gfx950"
 SOURCES = {
     "api.cpp": [],
     "attn_bf16.hip": [],
+    "attn_grp.hip": [],
     "attn_f32.hip": [],
     "lvsa_mask.hip": [],
     "draft.hip": ["-ffp-contract=off"],

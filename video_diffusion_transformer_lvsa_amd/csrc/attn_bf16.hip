@@ -428,9 +428,7 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_d128_kernel(AttnArgs a) {
   const int rest = logical / a.tiles_per_qb;
   int qb = rest % a.nqb;
   const int h = rest / a.nqb;
-  constexpr bool RASTER = MODE == MODE_T2D || MODE == MODE_T2DG;
-  constexpr bool GROUPS = MODE == MODE_GRP || MODE == MODE_T2DG;
-  if (RASTER) {
+  if (MODE == MODE_T2D) {
     // Raster Draft: consecutive workgroups (one XCD) take the same pool tile
     // of consecutive frames, whose top-k lists share more key blocks than
     // those of neighbouring tiles of one frame (measured: 1.2 % faster).
@@ -452,7 +450,7 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_d128_kernel(AttnArgs a) {
   bool q_in_blk = qrow < blk_end;
   bool q_valid = qrow < qend;
   bool no_queries = row_lo >= qend;
-  if (RASTER) {
+  if (MODE == MODE_T2D) {
     // Query block qb is a raster pool tile; slot s = (s / pw, s % pw).
     const BlkGeom gq = blk_geom(a, qb);
     const int s0 = qt * kBM;
@@ -485,7 +483,6 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_d128_kernel(AttnArgs a) {
     list = a.kv_idx + (size_t)base * a.max_kv;
     L = cnt * a.block_k;
   }
-  if (GROUPS) L = no_queries ? 0 : 16 * list_groups<MODE>(a, list, cnt);  // compacted key rows
   if (no_queries) L = 0;
   const int ntiles = (L + BN - 1) / BN;
 
@@ -557,21 +554,6 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_d128_kernel(AttnArgs a) {
       }
     }
   };
-  // Compacted walk: DMA instruction j fills group j (tile rows 16j .. 16j+15),
-  // one scalar base per group; rows past a group's valid count read zeros.
-  auto load_kg = [&](const GTile& t, int st) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      dma(Kr, st, 0, j, (t.full || dR < t.nv[j]) ? kdma : kInvalid, (unsigned)(t.base[j] * D * 2));
-  };
-  auto load_vg = [&](const GTile& t, int st) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const bool ok = t.full || dR < t.nv[j];
-      dma(Vr, st, 1, j, ok ? vdma : kInvalid, (unsigned)(t.base[j] * D * 2));
-      if (!t.full && dp == 0) ((unsigned char*)kval[st])[16 * j + dR] = ok ? 1 : 0;
-    }
-  };
   auto qk = [&](int st, f32x16 (&s)[NKB]) {
     const f32x16 zero = {};
 #pragma unroll
@@ -620,38 +602,17 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_d128_kernel(AttnArgs a) {
 
   f32x16 s[NKB], sn[NKB];
   int full_cur = 1;
-  // The key walk: tile descriptors of the virtual sequence, or of the
-  // compacted group sequence.
   TileStream ks;
-  GStream gs;
-  if (GROUPS) {
-    gs.slot = 0;
-    gs_seek<MODE>(gs, a, list, cnt);
-  } else {
-    stream_init<BN, MODE>(ks, a, list, cnt, 0);
-  }
-  auto next_tile = [&]() {
-    if constexpr (GROUPS) {
-      return gs_tile<MODE>(gs, a, list, cnt);
-    } else {
-      const TileD t = stream_tile<BN, MODE>(ks, a, L);
-      stream_next<BN, MODE>(ks, a, list, cnt);
-      return t;
-    }
-  };
-  auto load_kt = [&](const auto& t, int st) {
-    if constexpr (GROUPS) load_kg(t, st); else load_k(t, st);
-  };
-  auto load_vt = [&](const auto& t, int st) {
-    if constexpr (GROUPS) load_vg(t, st); else load_v(t, st);
-  };
-  decltype(next_tile()) tprev;
+  stream_init<BN, MODE>(ks, a, list, cnt, 0);
+  TileD tprev;
   if (ntiles > 0) {
-    const auto t0 = next_tile();
-    const auto t1 = next_tile();
-    load_kt(t0, 0);
-    load_vt(t0, 0);
-    load_kt(t1, 1);
+    const TileD t0 = stream_tile<BN, MODE>(ks, a, L);
+    stream_next<BN, MODE>(ks, a, list, cnt);
+    const TileD t1 = stream_tile<BN, MODE>(ks, a, L);
+    stream_next<BN, MODE>(ks, a, list, cnt);
+    load_k(t0, 0);
+    load_v(t0, 0);
+    load_k(t1, 1);
     full_cur = t0.full;
     tprev = t1;
   }
@@ -663,11 +624,12 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_d128_kernel(AttnArgs a) {
   auto step = [&](const int st, f32x16 (&cur)[NKB], f32x16 (&nxt)[NKB]) {
     // K of tile i+2 into the stage of tile i (its K was read last step);
     // V of tile i+1 into the other stage (its V was read last step).
-    const auto tk = next_tile();
-    const auto tv = tprev;
+    const TileD tk = stream_tile<BN, MODE>(ks, a, L);
+    stream_next<BN, MODE>(ks, a, list, cnt);
+    const TileD tv = tprev;
     tprev = tk;
-    load_kt(tk, st);
-    load_vt(tv, st ^ 1);
+    load_k(tk, st);
+    load_v(tv, st ^ 1);
 
     if (active) {
       if (!full_cur) {
@@ -754,7 +716,7 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_d128_kernel(AttnArgs a) {
 
   const float l_tot = half_sum(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  if (RASTER) {
+  if (MODE == MODE_T2D) {
     // Recompute the output row from an opaque copy of the lane id rather
     // than keep it live through the key walk.
     int lid = l32;
@@ -803,8 +765,6 @@ hipError_t launch_d128(const AttnArgs& a, hipStream_t s) {
   dim3 grid(a.total_tiles), block(kThreads);
   if (a.dense)
     hipLaunchKernelGGL((bsa_fwd_d128_kernel<MODE_DENSE, false>), grid, block, 0, s, a);
-  else if (a.block_k >= 64 && a.block_k % 16 == 0 && a.block_valid)
-    hipLaunchKernelGGL((bsa_fwd_d128_kernel<MODE_GRP, true>), grid, block, 0, s, a);
   else if (a.block_k >= 64 && a.block_valid)
     hipLaunchKernelGGL((bsa_fwd_d128_kernel<MODE_LIST, true>), grid, block, 0, s, a);
   else if (a.block_k >= 64)
@@ -816,10 +776,7 @@ hipError_t launch_d128(const AttnArgs& a, hipStream_t s) {
 
 hipError_t launch_draft_attn_bf16(const AttnArgs& a, hipStream_t s) {
   if (a.total_tiles == 0) return hipSuccess;
-  if (a.pw == 16)
-    hipLaunchKernelGGL((bsa_fwd_d128_kernel<MODE_T2DG, false>), dim3(a.total_tiles), dim3(kThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL((bsa_fwd_d128_kernel<MODE_T2D, false>), dim3(a.total_tiles), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL((bsa_fwd_d128_kernel<MODE_T2D, false>), dim3(a.total_tiles), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

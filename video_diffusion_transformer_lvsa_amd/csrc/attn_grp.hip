@@ -1,0 +1,432 @@
+// Block-sparse softmax attention forward for Draft Attention's block lists,
+// bf16 in, fp32 out, d = 128, on the gfx950 matrix cores, with a compacted
+// key walk.
+//
+// What it computes: Draft Attention's block-sparse execution (the article's
+// block-size and reorder paragraphs): every query row of a query block
+// attends to the valid keys of the KV blocks listed for it, O = softmax(scale
+// * Q Kᵀ) V over those keys only, on the reordered tokens (blocks with
+// per-block valid counts, MODE_GRP) or in place on the raster [t, h, w]
+// layout where a block is a pool tile 16 tokens wide (MODE_T2DG).
+//
+// Same algorithm, LDS layouts, operand layouts and software pipeline as
+// bsa_fwd_d128_kernel (attn_bf16.hip, whose header describes them), with one
+// difference: the key walk lists each block's valid rows only, as groups of
+// up to 16 consecutive physical rows, and a 64-key tile is four consecutive
+// groups (attn_tiles.h, GTile / GStream), so the empty part of a partly
+// valid edge block costs no tile. One DMA instruction loads one group with a
+// scalar base offset. Both layouts produce the same groups in the same order,
+// so the reorder and raster paths agree bit for bit.
+//
+// A kernel of its own so that the LVSA and dense launches keep their code:
+// their L2 reuse depends on every workgroup of a frame walking the same list
+// in step, which small changes of the instruction schedule were measured to
+// upset (L2 hit rate 96 % -> 46 % on the 14B LVSA workload).
+#include "attn_tiles.h"
+
+namespace lvsa {
+namespace {
+
+__device__ __forceinline__ int gv_swz(int x) { return 4 * x + 2 * (x >> 1); }
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+
+template <int MODE, bool SKIP>
+__global__ __launch_bounds__(kThreads, 2) void bsa_fwd_d128_grp_kernel(AttnArgs a) {
+  constexpr int D = 128, BN = 64, KSTEPS = 8, NKB = 2, PVSTEPS = 4, NDB = 4;
+  constexpr int TILE = BN * D * 2;  // 16 KB per K or V tile
+  // Four separate LDS objects (K and V of two stages) so the compiler can see
+  // that reading one stage does not wait for the loads filling the other.
+  __shared__ __attribute__((aligned(1024))) unsigned char ks0[TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char ks1[TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char vs0[TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char vs1[TILE];
+  __shared__ unsigned int kval[2][BN / 4];
+  auto kbuf = [&](int st) -> unsigned char* { return st == 0 ? ks0 : ks1; };
+  auto vbuf = [&](int st) -> unsigned char* { return st == 0 ? vs0 : vs1; };
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = lane >> 5;
+  const int l32 = lane & 31;
+
+  const int G = a.total_tiles;
+  const int w = blockIdx.x;
+  const int xcd = w & 7, idx = w >> 3, q8 = G >> 3, r8 = G & 7;
+  const int logical = (xcd < r8 ? xcd * (q8 + 1) : r8 * (q8 + 1) + (xcd - r8) * q8) + idx;
+  const int qt = logical % a.tiles_per_qb;
+  const int rest = logical / a.tiles_per_qb;
+  int qb = rest % a.nqb;
+  const int h = rest / a.nqb;
+  constexpr bool RASTER = MODE == MODE_T2D || MODE == MODE_T2DG;
+  constexpr bool GROUPS = MODE == MODE_GRP || MODE == MODE_T2DG;
+  if (RASTER) {
+    // Raster Draft: consecutive workgroups (one XCD) take the same pool tile
+    // of consecutive frames, whose top-k lists share more key blocks than
+    // those of neighbouring tiles of one frame (measured: 1.2 % faster).
+    const int per = a.nbh * a.nbw, nt = a.nqb / per;
+    qb = (qb % nt) * per + qb / nt;
+  }
+
+  const int blk_lo = qb * a.block_q;
+  const int blk_end = min(blk_lo + a.block_q, a.n);
+  int qlim = a.block_q;
+  if (a.block_valid) {
+    int bv = a.block_valid[qb];
+    qlim = bv < 0 ? 0 : (bv < qlim ? bv : qlim);
+  }
+  const int qend = min(blk_lo + qlim, blk_end);
+  const int row_lo = blk_lo + qt * kBM;
+  int qrow = row_lo + wave * 32 + l32;
+  bool active = !SKIP || row_lo + wave * 32 < qend;
+  bool q_in_blk = qrow < blk_end;
+  bool q_valid = qrow < qend;
+  bool no_queries = row_lo >= qend;
+  if (RASTER) {
+    // Query block qb is a raster pool tile; slot s = (s / pw, s % pw).
+    const BlkGeom gq = blk_geom(a, qb);
+    const int s0 = qt * kBM;
+    const int slot = s0 + wave * 32 + l32;
+    const int hi = slot >> a.lpw, wi = slot & (a.pw - 1);
+    q_valid = slot < a.block_q && hi < gq.vh && wi < gq.vw;
+    q_in_blk = q_valid;
+    qrow = q_valid ? gq.tok + hi * a.gW + wi : 0;
+    active = !SKIP || ((s0 + wave * 32) >> a.lpw) < gq.vh;
+    no_queries = (s0 >> a.lpw) >= gq.vh;
+  }
+
+  const size_t head_off = (size_t)h * (size_t)a.n * D;
+  const int head_bytes = a.n * D * 2;
+  const __amdgpu_buffer_rsrc_t Qr =
+      __builtin_amdgcn_make_buffer_rsrc((void*)((const uint16_t*)a.q + head_off), (short)0, head_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t Kr =
+      __builtin_amdgcn_make_buffer_rsrc((void*)((const uint16_t*)a.k + head_off), (short)0, head_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t Vr =
+      __builtin_amdgcn_make_buffer_rsrc((void*)((const uint16_t*)a.v + head_off), (short)0, head_bytes, 0x00020000);
+  float* __restrict__ Oh = a.o + head_off;
+
+  const int32_t* list = nullptr;
+  int cnt = 0, L = a.n;
+  if (MODE != MODE_DENSE) {
+    const int hm = a.mask_heads > 1 ? h : 0;
+    const int base = hm * a.nqb + qb;
+    cnt = a.kv_cnt[base];
+    cnt = cnt < 0 ? 0 : (cnt > a.max_kv ? a.max_kv : cnt);
+    list = a.kv_idx + (size_t)base * a.max_kv;
+    L = cnt * a.block_k;
+  }
+  if (GROUPS) L = no_queries ? 0 : 16 * list_groups<MODE>(a, list, cnt);  // compacted key rows
+  if (no_queries) L = 0;
+  const int ntiles = (L + BN - 1) / BN;
+
+  bf16x8 qreg[KSTEPS];
+#pragma unroll
+  for (int kk = 0; kk < KSTEPS; ++kk) {
+    const unsigned off = q_valid ? (unsigned)((qrow * D + 16 * kk + 8 * half) * 2) : kInvalid;
+    qreg[kk] = __builtin_bit_cast(bf16x8, bload(Qr, off));
+  }
+
+  // DMA roles: instruction j of wave `wave` fills tile rows 16j + 4*wave .. +3;
+  // lane writes row 16j + dR, LDS chunk dp.
+  const int dR = 4 * wave + (lane >> 4);
+  const int dp = lane & 15;
+  const unsigned kdma = (unsigned)(dR * 256 + 16 * (dp ^ (dR & 15)));
+  const unsigned vdma = (unsigned)(dR * 256 + 16 * (dp ^ gv_swz(dR & 3)));
+
+  // LDS read addresses (bytes inside a stage). K: row kb*32 + l32, chunk 2kk + half.
+  unsigned kra[KSTEPS];
+#pragma unroll
+  for (int kk = 0; kk < KSTEPS; ++kk) kra[kk] = (unsigned)(l32 * 256 + 16 * ((2 * kk + half) ^ (l32 & 15)));
+  // Vᵀ via transpose reads: lane (group g = lane/16, i = lane%16) reads keys
+  // 16kk + 8s + 4*(g/2) + i/4, channels 32db + 16*(g%2) + 4*(i%4) .. +3.
+  const int ti = lane & 15, tg = lane >> 4;
+  unsigned vra[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+    vra[db] = (unsigned)((4 * (tg >> 1) + (ti >> 2)) * 256 +
+                         16 * ((4 * db + 2 * (tg & 1) + ((ti & 3) >> 1)) ^ gv_swz(ti >> 2)) + 8 * (ti & 1));
+
+  // A tile whose 64 rows are valid and are 4 runs of 16 consecutive rows of
+  // K/V (one run per DMA instruction) loads with one scalar offset per run.
+  // All BN rows valid and physically consecutive from base0: one run, or two
+  // runs of adjacent blocks (then base1 == base0).
+  auto simple = [&](const TileD& t) {
+    return MODE == MODE_T2D ? (t.full && a.pw == 16) : (t.full && (t.bnd >= BN || t.base1 == t.base0));
+  };
+  const unsigned run_bytes = MODE == MODE_T2D ? (unsigned)a.gW * D * 2 : 4096u;
+  auto dma = [&](__amdgpu_buffer_rsrc_t r, int st, int kind, int j, unsigned voff, unsigned soff) {
+    unsigned char* dst = (kind == 0 ? kbuf(st) : vbuf(st)) + 4096 * j + 1024 * wave;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, voff, soff, 0, 0);
+  };
+  auto load_k = [&](const TileD& t, int st) {
+    if (simple(t)) {
+      const unsigned so = (unsigned)(t.base0 * D * 2);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dma(Kr, st, 0, j, kdma, so + run_bytes * j);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int R = 16 * j + dR;
+        const int p = tile_row<BN, MODE>(a, t, list, cnt, R);
+        dma(Kr, st, 0, j, p >= 0 ? (unsigned)(p * 256 + 16 * (dp ^ (R & 15))) : kInvalid, 0u);
+      }
+    }
+  };
+  auto load_v = [&](const TileD& t, int st) {
+    if (simple(t)) {
+      const unsigned so = (unsigned)(t.base0 * D * 2);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dma(Vr, st, 1, j, vdma, so + run_bytes * j);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int R = 16 * j + dR;
+        const int p = tile_row<BN, MODE>(a, t, list, cnt, R);
+        dma(Vr, st, 1, j, p >= 0 ? (unsigned)(p * 256 + 16 * (dp ^ gv_swz(R & 3))) : kInvalid, 0u);
+        if (dp == 0) ((unsigned char*)kval[st])[R] = p >= 0 ? 1 : 0;
+      }
+    }
+  };
+  // Compacted walk: DMA instruction j fills group j (tile rows 16j .. 16j+15),
+  // one scalar base per group; rows past a group's valid count read zeros.
+  auto load_kg = [&](const GTile& t, int st) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      dma(Kr, st, 0, j, (t.full || dR < t.nv[j]) ? kdma : kInvalid, (unsigned)(t.base[j] * D * 2));
+  };
+  auto load_vg = [&](const GTile& t, int st) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bool ok = t.full || dR < t.nv[j];
+      dma(Vr, st, 1, j, ok ? vdma : kInvalid, (unsigned)(t.base[j] * D * 2));
+      if (!t.full && dp == 0) ((unsigned char*)kval[st])[16 * j + dR] = ok ? 1 : 0;
+    }
+  };
+  auto qk = [&](int st, f32x16 (&s)[NKB]) {
+    const f32x16 zero = {};
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const bf16x8 A = __builtin_bit_cast(bf16x8, *(const u32x4*)(kbuf(st) + kb * 8192 + kra[kk]));
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, qreg[kk], kk == 0 ? zero : s[kb], 0, 0, 0);
+      }
+    }
+  };
+  auto wait_dma = [&]() { __builtin_amdgcn_s_waitcnt(0x0F70); };  // vmcnt(0)
+
+  f32x16 oacc[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[i][r] = 0.f;
+  float mc = -INFINITY;
+  float l_run = 0.f;
+  const float c = a.scale_log2;
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+
+  // exp2(s*c - m) of a tile's scores, rounded to bf16 into the B operand of
+  // the PV product; returns the lane's sum of the rounded values.
+  auto probs = [&](const f32x16 (&cur)[NKB], float m, bf16x8 (&pb)[PVSTEPS]) {
+    const float nm = (m == -INFINITY) ? 0.f : -m;
+    float t0 = 0.f, t1 = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < PVSTEPS; ++kk) {
+#pragma unroll
+      for (int j = 0; j < 8; j += 2) {
+        const float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(cur[kk >> 1][8 * (kk & 1) + j], c, nm));
+        const float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(cur[kk >> 1][8 * (kk & 1) + j + 1], c, nm));
+        const bf16x2 p2 = {(__bf16)x0, (__bf16)x1};
+        if (kk & 1)
+          t1 = __builtin_amdgcn_fdot2_f32_bf16(p2, ones, t1, false);
+        else
+          t0 = __builtin_amdgcn_fdot2_f32_bf16(p2, ones, t0, false);
+        pb[kk][j] = p2[0];
+        pb[kk][j + 1] = p2[1];
+      }
+    }
+    return t0 + t1;
+  };
+
+  f32x16 s[NKB], sn[NKB];
+  int full_cur = 1;
+  // The key walk: tile descriptors of the virtual sequence, or of the
+  // compacted group sequence.
+  TileStream ks;
+  GStream gs;
+  if (GROUPS) {
+    gs.slot = 0;
+    gs_seek<MODE>(gs, a, list, cnt);
+  } else {
+    stream_init<BN, MODE>(ks, a, list, cnt, 0);
+  }
+  auto next_tile = [&]() {
+    if constexpr (GROUPS) {
+      return gs_tile<MODE>(gs, a, list, cnt);
+    } else {
+      const TileD t = stream_tile<BN, MODE>(ks, a, L);
+      stream_next<BN, MODE>(ks, a, list, cnt);
+      return t;
+    }
+  };
+  auto load_kt = [&](const auto& t, int st) {
+    if constexpr (GROUPS) load_kg(t, st); else load_k(t, st);
+  };
+  auto load_vt = [&](const auto& t, int st) {
+    if constexpr (GROUPS) load_vg(t, st); else load_v(t, st);
+  };
+  decltype(next_tile()) tprev;
+  if (ntiles > 0) {
+    const auto t0 = next_tile();
+    const auto t1 = next_tile();
+    load_kt(t0, 0);
+    load_vt(t0, 0);
+    load_kt(t1, 1);
+    full_cur = t0.full;
+    tprev = t1;
+  }
+  wait_dma();
+  __syncthreads();
+  if (ntiles > 0 && active) qk(0, s);
+  __syncthreads();
+
+  auto step = [&](const int st, f32x16 (&cur)[NKB], f32x16 (&nxt)[NKB]) {
+    // K of tile i+2 into the stage of tile i (its K was read last step);
+    // V of tile i+1 into the other stage (its V was read last step).
+    const auto tk = next_tile();
+    const auto tv = tprev;
+    tprev = tk;
+    load_kt(tk, st);
+    load_vt(tv, st ^ 1);
+
+    if (active) {
+      if (!full_cur) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const unsigned f4 = kval[st][(kb * 32 + 8 * g + 4 * half) >> 2];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (((f4 >> (8 * i)) & 0xffu) == 0u) cur[kb][4 * g + i] = -INFINITY;
+          }
+      }
+
+      qk(st ^ 1, nxt);
+
+      // Probabilities against the running reference mc, with no row max:
+      // a lane whose probabilities of this tile sum to more than kSumBf16
+      // (or whose row has no reference yet) sends the wave through the
+      // exact path, which moves mc to the row max, rescales and recomputes.
+      bf16x8 pb[PVSTEPS];
+      float tl = probs(cur, mc, pb);
+      // Interleave the 16 Sᵀ MFMAs with their K reads (kept three ahead) and
+      // the softmax VALU work, which does not depend on them: a wave overlaps
+      // its own VALU work with its MFMAs only where the two are interleaved.
+      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i < 13) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+      }
+      if (__ballot(!(tl <= kSumBf16) || mc == -INFINITY) != 0ull) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, cur[kb][r]);
+        mx = half_max(mx) * c;
+        const float mc_new = fmaxf(mc, mx);
+        const float alpha = mc_new == mc ? 1.f : __builtin_amdgcn_exp2f(mc - mc_new);
+        mc = mc_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int i = 0; i < NDB; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
+        tl = probs(cur, mc, pb);
+      }
+      l_run += tl;
+
+#pragma unroll
+      for (int kk = 0; kk < PVSTEPS; ++kk) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          lds_u8* const vb = (lds_u8*)vbuf(st) + vra[db] + 16 * kk * 256;
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)vb);
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + 8 * 256));
+          const s16x4 both[2] = {lo, hi};
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, both), pb[kk], oacc[db], 0, 0, 0);
+        }
+      }
+      // Vᵀ reads run eight (four MFMAs) ahead of the PV MFMAs.
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i < 12) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+
+    }
+
+    full_cur = tv.full;
+    wait_dma();
+    __syncthreads();
+  };
+
+  int it = 0;
+  for (; it + 1 < ntiles; it += 2) {
+    step(0, s, sn);
+    step(1, sn, s);
+  }
+  if (it < ntiles) step(0, s, sn);
+
+  const float l_tot = half_sum(l_run);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (RASTER) {
+    // Recompute the output row from an opaque copy of the lane id rather
+    // than keep it live through the key walk.
+    int lid = l32;
+    asm volatile("" : "+v"(lid));
+    const BlkGeom gq = blk_geom(a, qb);
+    const int slot = qt * kBM + wave * 32 + lid;
+    const int hi = slot >> a.lpw, wi = slot & (a.pw - 1);
+    q_valid = slot < a.block_q && hi < gq.vh && wi < gq.vw;
+    q_in_blk = q_valid;
+    qrow = q_valid ? gq.tok + hi * a.gW + wi : 0;
+  }
+  if (q_in_blk) {
+    float* orow = Oh + (size_t)qrow * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = 32 * db + 8 * g + 4 * half;
+        float4 v;
+        if (q_valid) {
+          v = make_float4(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv, oacc[db][4 * g + 2] * inv,
+                          oacc[db][4 * g + 3] * inv);
+        } else {
+          v = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+        *(float4*)(orow + d0) = v;
+      }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_grp_bf16(const AttnArgs& a, hipStream_t s) {
+  if (a.total_tiles == 0) return hipSuccess;
+  if (a.tile2d)
+    hipLaunchKernelGGL((bsa_fwd_d128_grp_kernel<MODE_T2DG, false>), dim3(a.total_tiles), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((bsa_fwd_d128_grp_kernel<MODE_GRP, true>), dim3(a.total_tiles), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace lvsa

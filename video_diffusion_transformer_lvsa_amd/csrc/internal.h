@@ -49,6 +49,10 @@ constexpr int kBM_F32 = 64;
 hipError_t launch_attn_bf16(const AttnArgs& a, int d, hipStream_t s);
 // Draft attention on the raster layout (d = 128, bf16): a.tile2d = 1.
 hipError_t launch_draft_attn_bf16(const AttnArgs& a, hipStream_t s);
+// d = 128 bf16 attention with the compacted key walk: lists over blocks with
+// per-block valid counts (block_k >= 64, a multiple of 16), or the raster
+// layout with pools 16 tokens wide (a.tile2d = 1).
+hipError_t launch_grp_bf16(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_f32(const AttnArgs& a, int d, hipStream_t s);
 // E4M3 codes (q, k row-major [heads, n, 128], v transposed [heads, 128, a.ldv])
 // with per-head dequantization factors qs, ks, vs (device arrays).
