@@ -64,8 +64,10 @@ __device__ __forceinline__ i32x8 lds_read32(const unsigned char* base, unsigned 
 }
 
 __device__ __forceinline__ unsigned int pack4_fp8(float a, float b, float c, float d) {
-  unsigned int w = 0u;
-  w = (unsigned int)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)w, false);
+  // The first conversion fills bytes 0-1 and keeps bytes 2-3 of its third
+  // operand, which the second conversion overwrites: any value serves, and
+  // the bits of a (dead once its row sum is taken) need no extra register.
+  unsigned int w = (unsigned int)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)__float_as_uint(a), false);
   w = (unsigned int)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, (int)w, true);
   return w;
 }
