@@ -170,6 +170,48 @@ def test_bf16_ragged_query_blocks(n, bq, bk, max_kv, mask_heads, sorted_lists):
     assert np.all(o[0, bq : 2 * bq] == 0)  # empty list of block 1 (head 0)
 
 
+@pytest.mark.parametrize("block,seed", [(128, 0), (64, 1), (192, 2)])
+def test_bf16_compacted_walk_edge_cases(block, seed):
+    """Block lists over blocks with per-block valid counts (the walk that
+    lists only each block's valid rows, in groups of 16): valid counts 0, 1,
+    15, 16, 17, 63, 64, a full block and others, lists with repeated,
+    negative and out-of-range entries, empty lists and counts above max_kv;
+    pad query rows (slots at or past a block's valid count) give 0."""
+    torch = _torch()
+    rng = np.random.default_rng(70 + seed)
+    heads, d = 2, 128
+    nb = 12
+    n = nb * block
+    q, k, v = (synth.bf16_round(rng.standard_normal((heads, n, d)).astype(np.float32) * sc) for sc in (1.5, 1.5, 1.0))
+    special = [0, 1, 15, 16, 17, 63, 64, block, block - 1, 33, 100 % block, 48]
+    bv = np.array(special[:nb], dtype=np.int32)
+    rng.shuffle(bv)
+    max_kv = 7
+    idx = rng.integers(-1, nb + 1, size=(heads, nb, max_kv)).astype(np.int32)
+    cnt = rng.integers(0, max_kv + 1, size=(heads, nb)).astype(np.int32)
+    idx[0, 0, :3] = idx[0, 0, 0]   # repeats count twice
+    cnt[0, 1] = 0                  # empty list
+    cnt[1, 2] = max_kv + 5         # clamped to max_kv
+    idx[1, 3, :] = np.argsort(bv)[:max_kv]  # the emptiest blocks
+    cnt[1, 3] = max_kv
+    note(f"compacted walk edge cases block={block}")
+    o = to_host(_lib.block_sparse_attn_fwd(to_dev(q), to_dev(k), to_dev(v), block, block, torch.from_numpy(idx).cuda(),
+                                           torch.from_numpy(cnt).cuda(), mask_heads=heads,
+                                           block_valid=torch.from_numpy(bv).cuda()))
+    cnt_o = np.minimum(cnt, max_kv)
+    clean = np.zeros_like(idx)
+    ccnt = np.zeros_like(cnt_o)
+    for h in range(heads):
+        for b in range(nb):
+            keep = [x for x in idx[h, b, : cnt_o[h, b]] if 0 <= x < nb]
+            clean[h, b, : len(keep)] = keep
+            ccnt[h, b] = len(keep)
+    ref = oracle.block_sparse_attention(q, k, v, block, block, clean, ccnt, mask_heads=heads, block_valid=bv)
+    assert_attn_close(o, ref, what=f"compacted walk block={block}")
+    for b in range(nb):
+        assert np.all(o[:, b * block + bv[b] : (b + 1) * block] == 0)  # pad query rows
+
+
 def test_bf16_closed_forms():
     torch = _torch()
     rng = np.random.default_rng(12)
@@ -258,6 +300,7 @@ def _draft_pipeline(q, k, v, T, H, W, ph, pw, sp):
     (3, 45, 80, 8, 16, 2, 128, 0.9),   # HunyuanVideo frame and pool, 3 frames
     (2, 13, 21, 8, 16, 2, 64, 0.5),    # ragged tiles both ways
     (2, 9, 30, 4, 8, 2, 128, 0.0),     # k = nb: equals dense
+    (2, 13, 21, 8, 8, 2, 128, 0.5),    # 64-token blocks with 64, 40 and 25 valid: groups of 16, 9 and 8 rows
 ])
 def test_draft_attention_small_all_rows(T, H, W, ph, pw, heads, d, sp):
     q, k, v = _bf16_inputs(17, heads, T, H, W, d)
@@ -361,12 +404,14 @@ def test_full_hunyuan_draft():
     out, op, o = _draft_pipeline(q, k, v, w.T, w.H, w.W, w.pool_h, w.pool_w, w.sparsity)
     g = oracle.draft_grid(w.T, w.H, w.W, w.pool_h, w.pool_w)
     perm, inv, bv = oracle.draft_permutation(g)
-    kv = to_host(out["kv_idx"])  # bit-exact vs the oracle: test_gpu_masks
-    cnt = to_host(out["kv_cnt"])
     rng = np.random.default_rng(300)
     rows = sample_frame_rows(rng, w.T, w.P, nframes=5, per_frame=64)
     heads = [0, 7, 23]
-    ref = oracle.draft_attention_original_order(q, k, v, perm, inv, bv, g.block_size, kv, cnt, heads=heads, rows=rows)
+    # the oracle's own mask for these heads (the GPU's lists must equal it)
+    kv, cnt, *_ = oracle.draft_mask(synth.bf16_to_f32(q[heads]), synth.bf16_to_f32(k[heads]), g, w.sparsity)
+    assert np.array_equal(to_host(out["kv_idx"])[heads], kv) and np.array_equal(to_host(out["kv_cnt"])[heads], cnt)
+    ref = oracle.draft_attention_original_order(q[heads], k[heads], v[heads], perm, inv, bv, g.block_size, kv, cnt,
+                                                rows=rows)
     got = to_host(o)[heads][:, rows]
     assert_attn_close(got, ref, what="hunyuan draft")
     del out, op, o
