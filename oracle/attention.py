@@ -142,9 +142,8 @@ def draft_attention_original_order(q, k, v, perm, inv_perm, block_valid, block_s
     for hi, h in enumerate(heads):
         for b in np.unique(qblk):
             sel = np.nonzero(qblk == b)[0]
-            keys = np.concatenate(
-                [perm[bb * block_size : bb * block_size + int(block_valid[bb])] for bb in kv_idx[h, b, : int(kv_cnt[h, b])]]
-            )
+            parts = [perm[bb * block_size : bb * block_size + int(block_valid[bb])] for bb in kv_idx[h, b, : int(kv_cnt[h, b])]]
+            keys = np.concatenate(parts) if parts else np.zeros(0, dtype=np.int64)  # empty list: no keys
             out[hi, sel] = fn(to_f64(q[h, rows[sel]]), to_f64(k[h, keys]), to_f64(v[h, keys]), scale)
     return out
 

@@ -139,6 +139,32 @@ def test_draft_reorder_invariance():
     assert np.allclose(direct, want, rtol=1e-11, atol=1e-12)
 
 
+def test_draft_original_order_empty_and_repeated_lists():
+    """An empty key list gives an empty key set (output 0, the convention of
+    block_sparse_attention); a listed block repeated r times weighs its keys r
+    times; both equal the reordered computation mapped back."""
+    g, q, k, v, kv, cnt, perm, inv, bv = _draft_case()
+    kv, cnt = kv.copy(), cnt.copy()
+    cnt[0, 1] = 0
+    kv[1, 2, 1] = kv[1, 2, 0]
+    bs = g.block_size
+    direct = oracle.draft_attention_original_order(q, k, v, perm, inv, bv, bs, kv, cnt)
+    rows1 = perm[bs : bs + bv[1]]
+    assert np.all(direct[0, rows1] == 0)
+    o_perm = oracle.block_sparse_attention(_permute(q, perm), _permute(k, perm), _permute(v, perm), bs, bs, kv, cnt,
+                                           mask_heads=q.shape[0], block_valid=bv)
+    assert np.allclose(o_perm[:, inv], direct, rtol=1e-12, atol=1e-13)
+    # the repeated block: attention over the key multiset, written out with explicit weights
+    rows2 = perm[2 * bs : 2 * bs + bv[2]]
+    blocks = list(kv[1, 2, : cnt[1, 2]])
+    keys = np.concatenate([perm[b * bs : b * bs + bv[b]] for b in blocks])
+    qf, kf, vf = (synth.bf16_to_f32(x[1]).astype(np.float64) for x in (q, k, v))
+    s = qf[rows2] @ kf[keys].T / np.sqrt(q.shape[2])
+    w = np.exp(s - s.max(axis=1, keepdims=True))
+    want = (w @ vf[keys]) / w.sum(axis=1, keepdims=True)
+    assert np.allclose(direct[1, rows2], want, rtol=1e-12, atol=1e-13)
+
+
 def test_draft_all_blocks_equals_dense():
     g, q, k, v, *_ = _draft_case(sparsity=0.0)
     kv, cnt, *_ = oracle.draft_mask(synth.bf16_to_f32(q), synth.bf16_to_f32(k), g, 0.0)
