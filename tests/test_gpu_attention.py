@@ -212,6 +212,51 @@ def test_bf16_compacted_walk_edge_cases(block, seed):
         assert np.all(o[:, b * block + bv[b] : (b + 1) * block] == 0)  # pad query rows
 
 
+@pytest.mark.parametrize("path,max_kv", [("reorder", 1024), ("reorder", 1025), ("raster", 1024), ("raster", 1025)])
+def test_compacted_walk_list_capacity(path, max_kv):
+    """Key lists as long as the compacted walk's LDS slot table holds (1024
+    slots) and one slot longer (then the launch takes the kernels without the
+    table): full-length lists with repeated and invalid entries, short lists
+    and an empty one, on the reorder path (blocks with valid counts) and on
+    the raster path (pool tiles 16 wide, a ragged last column of tiles)."""
+    torch = _torch()
+    rng = np.random.default_rng(90 + (max_kv & 1) + (2 if path == "raster" else 0))
+    heads, d = 1, 128
+    if path == "reorder":
+        block, nb = 64, 8
+        n = nb * block
+        bv = np.array([64, 48, 64, 1, 64, 17, 64, 33], dtype=np.int32)
+    else:
+        T, H, W, ph, pw = 1, 16, 24, 8, 16
+        g = oracle.draft_grid(T, H, W, ph, pw)
+        perm, inv, bv = oracle.draft_permutation(g)
+        n, nb = T * H * W, g.nb
+    q, k, v = (synth.bf16_round(rng.standard_normal((heads, n, d)).astype(np.float32) * sc) for sc in (1.5, 1.5, 1.0))
+    idx = rng.integers(-1, nb + 1, size=(heads, nb, max_kv)).astype(np.int32)
+    lens = [max_kv, 0, max_kv - 3, 5, 1, max_kv // 2, 2, max_kv]
+    cnt = np.array([lens[:nb]], dtype=np.int32)
+    note(f"list capacity path={path} max_kv={max_kv}")
+    if path == "reorder":
+        o = _lib.block_sparse_attn_fwd(to_dev(q), to_dev(k), to_dev(v), block, block, torch.from_numpy(idx).cuda(),
+                                       torch.from_numpy(cnt).cuda(), mask_heads=heads,
+                                       block_valid=torch.from_numpy(bv).cuda())
+    else:
+        o = _lib.draft_attn_fwd(to_dev(q), to_dev(k), to_dev(v), T, H, W, ph, pw, torch.from_numpy(idx).cuda(),
+                                torch.from_numpy(cnt).cuda())
+    o = to_host(o)
+    clean = np.zeros_like(idx)
+    ccnt = np.zeros_like(cnt)
+    for b in range(nb):
+        keep = [x for x in idx[0, b, : cnt[0, b]] if 0 <= x < nb]
+        clean[0, b, : len(keep)] = keep
+        ccnt[0, b] = len(keep)
+    if path == "reorder":
+        ref = oracle.block_sparse_attention(q, k, v, block, block, clean, ccnt, mask_heads=heads, block_valid=bv)
+    else:
+        ref = oracle.draft_attention_original_order(q, k, v, perm, inv, bv, g.block_size, clean, ccnt)
+    assert_attn_close(o, ref, what=f"list capacity {path} max_kv={max_kv}")
+
+
 def test_bf16_closed_forms():
     torch = _torch()
     rng = np.random.default_rng(12)

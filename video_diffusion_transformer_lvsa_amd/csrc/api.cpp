@@ -159,7 +159,7 @@ int run_attn(lvsa::AttnArgs& a, int dt, int d, void* stream) {
   // Block lists with per-block valid counts (Draft on reordered tokens) walk
   // only the valid rows of each block.
   const bool grp = dt == LVSA_BF16 && d == 128 && !a.dense && a.block_valid && a.block_q == a.block_k &&
-                   a.block_k >= 64 && a.block_k % 16 == 0;
+                   a.block_k >= 64 && a.block_k % 16 == 0 && a.max_kv <= lvsa::kGrpMaxSlots;
   hipError_t e = grp ? lvsa::launch_grp_bf16(a, s)
                      : (dt == LVSA_BF16 ? lvsa::launch_attn_bf16(a, d, s) : lvsa::launch_attn_f32(a, d, s));
   return launched(e, "attention launch");
@@ -469,7 +469,8 @@ int draft_attn_fwd(const void* q, const void* k, const void* v, float* o, int dt
   rc = check_device();
   if (rc) return rc;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  return launched(pool_w == 16 ? lvsa::launch_grp_bf16(a, s) : lvsa::launch_draft_attn_bf16(a, s),
+  const bool grp = pool_w == 16 && max_kv <= lvsa::kGrpMaxSlots;
+  return launched(grp ? lvsa::launch_grp_bf16(a, s) : lvsa::launch_draft_attn_bf16(a, s),
                   "draft attention launch");
 }
 

@@ -193,84 +193,6 @@ struct GTile {
   int full;     // every group has 16 valid rows
 };
 
-struct GStream {
-  int slot;  // list slot of the next group
-  int g;     // next group inside that slot
-  int ng;    // groups of that slot (0: the list is exhausted)
-  int blk;   // its KV block
-  int lim;   // MODE_GRP: valid rows of the block; MODE_T2DG: valid columns
-  int tok;   // MODE_T2DG: first token of the block
-};
-
-// Groups of list slot `slot` (0 for an invalid entry or an empty block).
-template <int MODE>
-__device__ __forceinline__ int slot_groups(const AttnArgs& a, const int32_t* list, int cnt, int slot, int& blk,
-                                           int& lim, int& tok) {
-  blk = list_entry(a, list, cnt, slot);
-  tok = 0;
-  lim = 0;
-  if (blk < 0) return 0;
-  if (MODE == MODE_GRP) {
-    lim = block_lim(a, blk);
-    return (lim + 15) >> 4;
-  }
-  const BlkGeom geo = blk_geom(a, blk);
-  tok = geo.tok;
-  lim = geo.vw;
-  return geo.vw > 0 ? geo.vh : 0;
-}
-
-// Moves s to the first slot at or after s.slot that has groups.
-template <int MODE>
-__device__ __forceinline__ void gs_seek(GStream& s, const AttnArgs& a, const int32_t* list, int cnt) {
-  s.g = 0;
-  s.ng = 0;
-  while (s.slot < cnt) {
-    s.ng = slot_groups<MODE>(a, list, cnt, s.slot, s.blk, s.lim, s.tok);
-    if (s.ng > 0) return;
-    ++s.slot;
-  }
-}
-
-// Total groups of a list (the walk's length).
-template <int MODE>
-__device__ __forceinline__ int list_groups(const AttnArgs& a, const int32_t* list, int cnt) {
-  int total = 0;
-  for (int sl = 0; sl < cnt; ++sl) {
-    int blk, lim, tok;
-    total += slot_groups<MODE>(a, list, cnt, sl, blk, lim, tok);
-  }
-  return total;
-}
-
-// The next tile: four groups taken from s (empty groups past the end).
-template <int MODE>
-__device__ __forceinline__ GTile gs_tile(GStream& s, const AttnArgs& a, const int32_t* list, int cnt) {
-  GTile t;
-  t.full = 1;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    if (s.ng == 0) {
-      t.base[j] = 0;
-      t.nv[j] = 0;
-    } else {
-      if (MODE == MODE_GRP) {
-        t.base[j] = s.blk * a.block_k + 16 * s.g;
-        t.nv[j] = min(16, s.lim - 16 * s.g);
-      } else {
-        t.base[j] = s.tok + s.g * a.gW;
-        t.nv[j] = min(16, s.lim);
-      }
-      if (++s.g == s.ng) {
-        ++s.slot;
-        gs_seek<MODE>(s, a, list, cnt);
-      }
-    }
-    t.full &= (t.nv[j] == 16);
-  }
-  return t;
-}
-
 // Physical row of tile row r, or -1 if r is not a valid key.
 template <int BN, int MODE>
 __device__ __forceinline__ int tile_row(const AttnArgs& a, const TileD& t, const int32_t* list, int cnt, int r) {

@@ -53,6 +53,9 @@ hipError_t launch_draft_attn_bf16(const AttnArgs& a, hipStream_t s);
 // per-block valid counts (block_k >= 64, a multiple of 16), or the raster
 // layout with pools 16 tokens wide (a.tile2d = 1).
 hipError_t launch_grp_bf16(const AttnArgs& a, hipStream_t s);
+// Longest key list (max_kv) launch_grp_bf16 accepts: its workgroups hold the
+// list as an LDS table of this many slots.
+constexpr int kGrpMaxSlots = 1024;
 hipError_t launch_attn_f32(const AttnArgs& a, int d, hipStream_t s);
 // E4M3 codes (q, k row-major [heads, n, 128], v transposed [heads, 128, a.ldv])
 // with per-head dequantization factors qs, ks, vs (device arrays).
