@@ -38,6 +38,11 @@ METRIC = "block-sparse attn ms/call + effective TFLOP/s (% bf16 MFMA peak), 1 MI
 ATTN_SRC = os.path.join(ROOT, "video_diffusion_transformer_lvsa_amd", "csrc", "attn_bf16.hip")
 ATTN_FP8_SRC = os.path.join(ROOT, "video_diffusion_transformer_lvsa_amd", "csrc", "attn_fp8.hip")
 ATTN_GRP_SRC = os.path.join(ROOT, "video_diffusion_transformer_lvsa_amd", "csrc", "attn_grp.hip")
+# A bf16 LVSA call launches the full 128-row tiles of every frame
+# (attn_bf16.hip) and then the short frame tails, four frames per workgroup
+# (attn_grp.hip).
+LVSA_SRCS = (ATTN_SRC, ATTN_GRP_SRC)
+LVSA_KERNELS = ("bsa_fwd_d128_kernel<MODE_LIST, false>", "bsa_fwd_d128_grp_kernel<MODE_TAIL, true>")
 DRAFT_SRC = os.path.join(ROOT, "video_diffusion_transformer_lvsa_amd", "csrc", "draft.hip")
 
 WORKLOAD_NAMES = {
@@ -50,14 +55,18 @@ WORKLOAD_NAMES = {
 }
 
 
-def src_hash(path: str) -> str:
-    """Hash of a kernel source's code: comments and whitespace removed, so a
-    counter record stays valid across edits that change no code."""
-    with open(path) as f:
-        text = f.read()
-    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
-    text = re.sub(r"//[^\n]*", " ", text)
-    text = re.sub(r"\s+", "", text)
+def src_hash(*paths: str) -> str:
+    """Hash of the code of one or more kernel sources (a record of a call that
+    launches kernels from several files names them all): comments and
+    whitespace removed, so a counter record stays valid across edits that
+    change no code."""
+    text = ""
+    for path in paths:
+        with open(path) as f:
+            t = f.read()
+        t = re.sub(r"/\*.*?\*/", " ", t, flags=re.S)
+        t = re.sub(r"//[^\n]*", " ", t)
+        text += re.sub(r"\s+", "", t)
     return hashlib.sha256(text.encode()).hexdigest()[:16]
 
 
@@ -70,7 +79,7 @@ def lvsa_pairs(w, kv_cnt_host) -> int:
     return int(w.heads) * w.P * w.P * int(kv_cnt_host.sum())
 
 
-def _record(kind: str, workload: str, kernel_src: str):
+def _record(kind: str, workload: str, kernel_src):
     """A committed rocprofv3 summary (profiles/<kind>_<workload>.json) and a note
     of where it came from, if it was taken on the current kernel code; else
     (None, None). Its figures come from separate profiled runs, not this one."""
@@ -80,13 +89,14 @@ def _record(kind: str, workload: str, kernel_src: str):
         return None, None
     with open(path) as f:
         t = json.load(f)
-    if t.get("kernel_code_sha256_16") != src_hash(kernel_src):
+    srcs = (kernel_src,) if isinstance(kernel_src, str) else tuple(kernel_src)
+    if t.get("kernel_code_sha256_16") != src_hash(*srcs):
         return None, None
     return t, {"file": rel, "kernel_code_sha256_16": t["kernel_code_sha256_16"],
                "measured": "separate rocprofv3 runs of the commands in the file, not this run"}
 
 
-def traffic_for(workload: str, kernel_src: str):
+def traffic_for(workload: str, kernel_src):
     """(HBM bytes per launch, source) from the committed rocprofv3 --pmc summary."""
     t, src = _record("traffic", workload, kernel_src)
     return (None, None) if t is None else (t.get("hbm_bytes_per_launch"), src)
@@ -102,7 +112,7 @@ def oracle_threads() -> int:
         return len(os.sched_getaffinity(0))
 
 
-def counters_for(workload: str, kernel_src: str):
+def counters_for(workload: str, kernel_src):
     """(counter figures, source): clock, MFMA busy, L2 hit from the committed
     rocprofv3 summary, if it was taken on the current kernel code."""
     t, src = _record("counters", workload, kernel_src)
@@ -340,7 +350,7 @@ def run_lvsa(args, w):
         res["quantize_ms"] = round(quant_ms, 4)
         res["pct_fp8_peak"] = round(100.0 * achieved / PEAK_FP8_TFLOPS, 2)
     # the counter records were taken at the workload's own frame budget
-    traffic, tsrc = traffic_for(w.name + ("-fp8" if fp8 else ""), ATTN_FP8_SRC if fp8 else ATTN_SRC) \
+    traffic, tsrc = traffic_for(w.name + ("-fp8" if fp8 else ""), ATTN_FP8_SRC if fp8 else LVSA_SRCS) \
         if own_budget else (None, None)
     res["roofline"] = {
         "bound": "mfma",
@@ -349,11 +359,14 @@ def run_lvsa(args, w):
         "unit": "TFLOP/s",
         "frac": round(achieved / peak, 4),
         "traffic": traffic,
-        "kernel": "bsa_fwd_fp8_kernel<MODE_LIST, 4>" if fp8 else "bsa_fwd_d128_kernel<MODE_LIST, false>",
+        "kernel": "bsa_fwd_fp8_kernel<MODE_LIST, 4>" if fp8 else LVSA_KERNELS[0],
     }
+    if not fp8:
+        # achieved and traffic are per call: both launches of the call
+        res["roofline"]["launches_per_call"] = list(LVSA_KERNELS)
     if tsrc is not None:
         res["roofline"]["traffic_source"] = tsrc
-    ctr = counters_for(w.name + ("-fp8" if fp8 else ""), ATTN_FP8_SRC if fp8 else ATTN_SRC) if own_budget else None
+    ctr = counters_for(w.name + ("-fp8" if fp8 else ""), ATTN_FP8_SRC if fp8 else LVSA_SRCS) if own_budget else None
     if ctr is not None:
         res["counters"] = ctr
 
@@ -594,7 +607,8 @@ def _per_kernel(rows, counter: str):
 
 
 def _profiled_kernel(workload: str, fp8: bool, raster: bool = False):
-    """(source, kernel key in traces, label, traffic/counter key, algorithmic bytes per launch)."""
+    """(sources, kernel key in traces, label, traffic/counter key, algorithmic
+    bytes per call, keys of the call's other launches)."""
     from video_diffusion_transformer_lvsa_amd import synth
 
     w = synth.WORKLOADS[workload]
@@ -608,13 +622,12 @@ def _profiled_kernel(workload: str, fp8: bool, raster: bool = False):
     key = w.name + ("-raster" if raster else "") + ("-fp8" if fp8 else "")
     if fp8:
         mode = ("3", "MODE_T2D") if raster else ("1", "MODE_LIST")
-        return ATTN_FP8_SRC, f"bsa_fwd_fp8_kernel<{mode[0]}, 4>", f"bsa_fwd_fp8_kernel<{mode[1]}, 4>", key, alg
+        return (ATTN_FP8_SRC,), f"bsa_fwd_fp8_kernel<{mode[0]}, 4>", f"bsa_fwd_fp8_kernel<{mode[1]}, 4>", key, alg, ()
     if w.kind == "draft":
         tmpl, label = (("bsa_fwd_d128_grp_kernel<5, false>", "bsa_fwd_d128_grp_kernel<MODE_T2DG, false>") if raster
                        else ("bsa_fwd_d128_grp_kernel<4, true>", "bsa_fwd_d128_grp_kernel<MODE_GRP, true>"))
-        return ATTN_GRP_SRC, tmpl, label, key, alg
-    tmpl, label = "bsa_fwd_d128_kernel<1, false>", "bsa_fwd_d128_kernel<MODE_LIST, false>"
-    return ATTN_SRC, tmpl, label, key, alg
+        return (ATTN_GRP_SRC,), tmpl, label, key, alg, ()
+    return LVSA_SRCS, "bsa_fwd_d128_kernel<1, false>", LVSA_KERNELS[0], key, alg, ("bsa_fwd_d128_grp_kernel<6, true>",)
 
 
 def summarize(argv) -> int:
@@ -645,7 +658,7 @@ def summarize(argv) -> int:
         with open(a.out, "w") as f:
             f.write("\n".join(lines) + "\n")
         return 0
-    src, key, label, tkey, alg = _profiled_kernel(a.workload, a.fp8, a.no_reorder)
+    src, key, label, tkey, alg, extra = _profiled_kernel(a.workload, a.fp8, a.no_reorder)
     if a.what == "traffic":
         fr, wr = _per_kernel(_csv_in(a.fetch, "counter_collection.csv"), "FETCH_SIZE"), \
             _per_kernel(_csv_in(a.write, "counter_collection.csv"), "WRITE_SIZE")
@@ -657,62 +670,74 @@ def summarize(argv) -> int:
         cw = sum(wr[cal][:3]) / 3
         ff, fw = known_r / cf, known_w / cw
         mean = lambda v: sum(v) / len(v)
+        calls = (key,) + tuple(e for e in extra if e in fr and e in wr)
         t = {"kernel": label, "workload": WORKLOAD_NAMES[a.workload] + ("-raster" if a.no_reorder else "")
              + ("-fp8" if a.fp8 else ""),
-             "kernel_code_sha256_16": src_hash(src),
+             "kernel_code_sha256_16": src_hash(*src),
              "fetch_size_kib_raw": mean(fr[key]), "write_size_kib_raw": mean(wr[key]),
              "copy_calibration": {"kernel": f"token_permute_kernel (identity map, {a.calib_copy_mb} MiB)",
                                   "read_kib_known": known_r, "fetch_size_kib": cf, "write_kib_known": known_w,
                                   "write_size_kib": cw, "fetch_factor": ff, "write_factor": fw},
-             "hbm_fetch_bytes_per_launch": mean(fr[key]) * ff * 1024,
-             "hbm_write_bytes_per_launch": mean(wr[key]) * fw * 1024,
+             # per call: the dominant kernel plus the call's other launches
+             "hbm_fetch_bytes_per_launch": sum(mean(fr[k]) for k in calls) * ff * 1024,
+             "hbm_write_bytes_per_launch": sum(mean(wr[k]) for k in calls) * fw * 1024,
              "algorithmic_bytes_per_launch": alg,
              "note": "FETCH_SIZE counts L2 misses, served by MALL or HBM",
              "other_kernels_bytes_per_launch": {
                  k: {"read": mean(fr[k] if k != cal else fr[k][3:] or fr[k]) * ff * 1024,
                      "write": mean(wr[k] if k != cal else wr[k][3:] or wr[k]) * fw * 1024}
-                 for k in sorted(set(fr) & set(wr)) if k != key and (k != cal or len(fr[k]) > 3)},
+                 for k in sorted(set(fr) & set(wr)) if k not in calls and (k != cal or len(fr[k]) > 3)},
              "commands": a.cmd}
+        if len(calls) > 1:
+            t["launches_per_call"] = {k: {"read": mean(fr[k]) * ff * 1024, "write": mean(wr[k]) * fw * 1024}
+                                      for k in calls}
         t["hbm_bytes_per_launch"] = t["hbm_fetch_bytes_per_launch"] + t["hbm_write_bytes_per_launch"]
         out = a.out or os.path.join(ROOT, "profiles", f"traffic_{tkey}.json")
     else:
-        got = {}
-        for d in a.passes:
-            rows = _csv_in(d, "counter_collection.csv")
-            for r in rows:
-                if _kernel_key(r["Kernel_Name"]) != key:
-                    continue
-                did = (d, r["Dispatch_Id"])
-                e = got.setdefault(r["Counter_Name"], {})
-                e[did] = float(r["Counter_Value"])
-                got.setdefault("_dur", {})[did] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
-        m = {c: sum(v.values()) / len(v) for c, v in got.items()}
-        xcd, simds = 8, 1024
-        clk = m["GRBM_GUI_ACTIVE"] / xcd / m["_dur"]
-        cyc = m["GRBM_GUI_ACTIVE"] / xcd
+        def metrics(kname):
+            got = {}
+            for d in a.passes:
+                rows = _csv_in(d, "counter_collection.csv")
+                for r in rows:
+                    if _kernel_key(r["Kernel_Name"]) != kname:
+                        continue
+                    did = (d, r["Dispatch_Id"])
+                    e = got.setdefault(r["Counter_Name"], {})
+                    e[did] = float(r["Counter_Value"])
+                    got.setdefault("_dur", {})[did] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+            if not got:
+                return None
+            m = {c: sum(v.values()) / len(v) for c, v in got.items()}
+            xcd, simds = 8, 1024
+            clk = m["GRBM_GUI_ACTIVE"] / xcd / m["_dur"]
+            cyc = m["GRBM_GUI_ACTIVE"] / xcd
+            mops = "SQ_INSTS_VALU_MFMA_MOPS_F8" if a.fp8 else "SQ_INSTS_VALU_MFMA_MOPS_BF16"
+            met = {"duration_ms_under_counters": round(m["_dur"] * 1e3, 2), "shader_clock_ghz": round(clk / 1e9, 3)}
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in m:
+                met["mfma_busy_frac"] = round(m["SQ_VALU_MFMA_BUSY_CYCLES"] / simds / cyc, 4)
+            if mops in m:
+                met["matrix_core_flop_per_launch"] = m[mops] * 512
+            if "SQ_INSTS_MFMA" in m:
+                met["mfma_insts_per_launch"] = m["SQ_INSTS_MFMA"]
+                if "SQ_INSTS_VALU" in m:
+                    met["other_valu_per_mfma"] = round((m["SQ_INSTS_VALU"] - m["SQ_INSTS_MFMA"]) / m["SQ_INSTS_MFMA"], 3)
+            if "SQ_WAIT_INST_ANY" in m and "SQ_WAVE_CYCLES" in m:
+                met["dependency_wait_frac"] = round(m["SQ_WAIT_INST_ANY"] / m["SQ_WAVE_CYCLES"], 4)
+            if "SQ_VALU_MFMA_COEXEC_CYCLES" in m:
+                met["valu_mfma_coexec_frac"] = round(m["SQ_VALU_MFMA_COEXEC_CYCLES"] / simds / cyc, 4)
+            if "TCC_HIT_sum" in m and "TCC_MISS_sum" in m:
+                met["l2_hit_rate"] = round(m["TCC_HIT_sum"] / (m["TCC_HIT_sum"] + m["TCC_MISS_sum"]), 4)
+            if "SQ_LDS_BANK_CONFLICT" in m:
+                met["lds_bank_conflicts"] = m["SQ_LDS_BANK_CONFLICT"]
+            if "SQ_INSTS_LDS" in m:
+                met["lds_insts_per_launch"] = m["SQ_INSTS_LDS"]
+            return met
+
+        met = metrics(key)
         mops = "SQ_INSTS_VALU_MFMA_MOPS_F8" if a.fp8 else "SQ_INSTS_VALU_MFMA_MOPS_BF16"
-        met = {"duration_ms_under_counters": round(m["_dur"] * 1e3, 2), "shader_clock_ghz": round(clk / 1e9, 3)}
-        if "SQ_VALU_MFMA_BUSY_CYCLES" in m:
-            met["mfma_busy_frac"] = round(m["SQ_VALU_MFMA_BUSY_CYCLES"] / simds / cyc, 4)
-        if mops in m:
-            met["matrix_core_flop_per_launch"] = m[mops] * 512
-        if "SQ_INSTS_MFMA" in m:
-            met["mfma_insts_per_launch"] = m["SQ_INSTS_MFMA"]
-            if "SQ_INSTS_VALU" in m:
-                met["other_valu_per_mfma"] = round((m["SQ_INSTS_VALU"] - m["SQ_INSTS_MFMA"]) / m["SQ_INSTS_MFMA"], 3)
-        if "SQ_WAIT_INST_ANY" in m and "SQ_WAVE_CYCLES" in m:
-            met["dependency_wait_frac"] = round(m["SQ_WAIT_INST_ANY"] / m["SQ_WAVE_CYCLES"], 4)
-        if "SQ_VALU_MFMA_COEXEC_CYCLES" in m:
-            met["valu_mfma_coexec_frac"] = round(m["SQ_VALU_MFMA_COEXEC_CYCLES"] / simds / cyc, 4)
-        if "TCC_HIT_sum" in m and "TCC_MISS_sum" in m:
-            met["l2_hit_rate"] = round(m["TCC_HIT_sum"] / (m["TCC_HIT_sum"] + m["TCC_MISS_sum"]), 4)
-        if "SQ_LDS_BANK_CONFLICT" in m:
-            met["lds_bank_conflicts"] = m["SQ_LDS_BANK_CONFLICT"]
-        if "SQ_INSTS_LDS" in m:
-            met["lds_insts_per_launch"] = m["SQ_INSTS_LDS"]
         t = {"kernel": label, "workload": WORKLOAD_NAMES[a.workload] + ("-raster" if a.no_reorder else "")
              + ("-fp8" if a.fp8 else ""),
-             "kernel_code_sha256_16": src_hash(src), "metrics": met,
+             "kernel_code_sha256_16": src_hash(*src), "metrics": met,
              "derivation": {"shader_clock_ghz": "GRBM_GUI_ACTIVE / 8 XCDs / dispatch duration",
                             "mfma_busy_frac": "SQ_VALU_MFMA_BUSY_CYCLES / 1024 SIMDs / (GRBM_GUI_ACTIVE / 8)",
                             "matrix_core_flop_per_launch": mops + " x 512",
@@ -721,6 +746,10 @@ def summarize(argv) -> int:
                             "valu_mfma_coexec_frac": "SQ_VALU_MFMA_COEXEC_CYCLES / 1024 / (GRBM_GUI_ACTIVE / 8)",
                             "l2_hit_rate": "TCC_HIT_sum / (TCC_HIT_sum + TCC_MISS_sum)"},
              "commands": a.cmd}
+        others = {e: metrics(e) for e in extra}
+        others = {e: v for e, v in others.items() if v is not None}
+        if others:
+            t["other_launches_per_call"] = others
         out = a.out or os.path.join(ROOT, "profiles", f"counters_{tkey}.json")
     with open(out, "w") as f:
         json.dump(t, f, indent=1)

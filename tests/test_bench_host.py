@@ -18,6 +18,7 @@ COLS = ["Correlation_Id", "Dispatch_Id", "Agent_Id", "Queue_Id", "Process_Id", "
         "Kernel_Name", "Workgroup_Size", "LDS_Block_Size", "Scratch_Size", "VGPR_Count", "Accum_VGPR_Count",
         "SGPR_Count", "Counter_Name", "Counter_Value", "Start_Timestamp", "End_Timestamp"]
 ATTN = "void lvsa::(anonymous namespace)::bsa_fwd_d128_kernel<1, false>(lvsa::AttnArgs)"
+TAIL = "void lvsa::(anonymous namespace)::bsa_fwd_d128_grp_kernel<6, true>(lvsa::AttnArgs)"
 COPY = "void lvsa::(anonymous namespace)::token_permute_kernel(u32x4 const*, u32x4*, int const*, int, int, int)"
 
 
@@ -52,9 +53,13 @@ def test_traffic_summary_scales_by_the_copy_calibration(tmp_path):
     known_r, known_w = (rows * 256 + rows * 4) / 1024, rows * 256 / 1024
     # the counter reads half the copy's bytes on fetch and all of them on write
     fetch = [(COPY, "FETCH_SIZE", known_r / 2, 0, 1)] * 3 + [(ATTN, "FETCH_SIZE", 1000.0, 0, 1),
-                                                             (ATTN, "FETCH_SIZE", 3000.0, 0, 1)]
+                                                             (ATTN, "FETCH_SIZE", 3000.0, 0, 1),
+                                                             (TAIL, "FETCH_SIZE", 50.0, 0, 1),
+                                                             (TAIL, "FETCH_SIZE", 150.0, 0, 1)]
     write = [(COPY, "WRITE_SIZE", known_w, 0, 1)] * 3 + [(ATTN, "WRITE_SIZE", 10.0, 0, 1),
-                                                         (ATTN, "WRITE_SIZE", 30.0, 0, 1)]
+                                                         (ATTN, "WRITE_SIZE", 30.0, 0, 1),
+                                                         (TAIL, "WRITE_SIZE", 2.0, 0, 1),
+                                                         (TAIL, "WRITE_SIZE", 4.0, 0, 1)]
     _write(tmp_path / "f", fetch)
     _write(tmp_path / "w", write)
     out = tmp_path / "t.json"
@@ -63,12 +68,15 @@ def test_traffic_summary_scales_by_the_copy_calibration(tmp_path):
     t = json.loads(out.read_text())
     assert t["copy_calibration"]["fetch_factor"] == pytest.approx(2.0)
     assert t["copy_calibration"]["write_factor"] == pytest.approx(1.0)
-    assert t["hbm_fetch_bytes_per_launch"] == pytest.approx(2000.0 * 2 * 1024)
-    assert t["hbm_write_bytes_per_launch"] == pytest.approx(20.0 * 1024)
+    # per call: the full-tile launch and the frame-tail launch
+    assert t["hbm_fetch_bytes_per_launch"] == pytest.approx((2000.0 + 100.0) * 2 * 1024)
+    assert t["hbm_write_bytes_per_launch"] == pytest.approx((20.0 + 3.0) * 1024)
+    assert t["launches_per_call"]["bsa_fwd_d128_grp_kernel<6, true>"]["read"] == pytest.approx(100.0 * 2 * 1024)
     assert t["hbm_bytes_per_launch"] == pytest.approx(t["hbm_fetch_bytes_per_launch"] + t["hbm_write_bytes_per_launch"])
     # Q, K, V read once (bf16) and O written once (fp32)
     assert t["algorithmic_bytes_per_launch"] == 3 * 12 * 196560 * 128 * 2 + 12 * 196560 * 128 * 4
-    assert t["kernel_code_sha256_16"] == bench.src_hash(bench.ATTN_SRC)
+    assert t["kernel_code_sha256_16"] == bench.src_hash(*bench.LVSA_SRCS)
+    assert bench.src_hash(*bench.LVSA_SRCS) != bench.src_hash(bench.ATTN_SRC)
 
 
 def test_counter_summary(tmp_path):
@@ -78,13 +86,15 @@ def test_counter_summary(tmp_path):
          (ATTN, "SQ_INSTS_MFMA", 100.0, 0, dur_ns), (ATTN, "SQ_INSTS_VALU", 500.0, 0, dur_ns),
          (ATTN, "SQ_INSTS_VALU_MFMA_MOPS_BF16", 4.0, 0, dur_ns)]
     m = [(ATTN, "GRBM_GUI_ACTIVE", gui, 0, dur_ns), (ATTN, "TCC_HIT_sum", 90.0, 0, dur_ns),
-         (ATTN, "TCC_MISS_sum", 10.0, 0, dur_ns)]
+         (ATTN, "TCC_MISS_sum", 10.0, 0, dur_ns), (TAIL, "GRBM_GUI_ACTIVE", gui / 4, 0, dur_ns // 4)]
     _write(tmp_path / "a", a)
     _write(tmp_path / "m", m)
     out = tmp_path / "c.json"
     assert bench.summarize(["counters", "--workload", "wan1.3b-6x", "--passes", str(tmp_path / "a"),
                             str(tmp_path / "m"), "--out", str(out)]) == 0
-    met = json.loads(out.read_text())["metrics"]
+    rec = json.loads(out.read_text())
+    met = rec["metrics"]
+    assert rec["other_launches_per_call"]["bsa_fwd_d128_grp_kernel<6, true>"]["duration_ms_under_counters"] == 0.5
     assert met["shader_clock_ghz"] == pytest.approx(2.0)
     assert met["mfma_busy_frac"] == pytest.approx(0.5)
     assert met["other_valu_per_mfma"] == pytest.approx(4.0)

@@ -73,6 +73,13 @@ SMALL_LVSA = [
     (9, 5, 4, 2, 128, 4, 3, 4),     # P = 20 < 64: blocks smaller than a tile
     (4, 3, 3, 1, 64, 2, 1, 2),      # P = 9
     (12, 30, 52, 2, 128, 5, 3, 4),  # Wan frame size, short video
+    # frames that end in a short tile (at most 32 rows): full tiles and the
+    # tails of four frames per workgroup are separate launches
+    (5, 10, 14, 2, 128, 3, 2, 2),   # P = 140 = 128 + 12; frame groups of 4 and 1
+    (7, 8, 20, 2, 128, 4, 2, 3),    # P = 160 = 128 + 32; groups of 4 and 3
+    (1, 12, 13, 1, 128, 1, 1, 1),   # P = 156, one frame
+    (6, 11, 12, 2, 128, 6, 3, 2),   # P = 132 = 128 + 4, every frame listed
+    (3, 10, 17, 1, 128, 2, 1, 2),   # P = 170 = 128 + 42: tail longer than a wave, one launch
 ]
 
 
@@ -125,6 +132,44 @@ def test_bf16_block_list_edge_cases():
     ref = oracle.block_sparse_attention(q, k, v, bq, bk, clean, ccnt, mask_heads=heads, scale=scale)
     assert_attn_close(o, ref, what="edge")
     assert np.all(o[1, bq : 2 * bq] == 0)
+
+
+@pytest.mark.parametrize("T,P,max_kv,mask_heads", [
+    (9, 152, 6, 2),    # per-head lists, groups of 4, 4, 1
+    (5, 280, 64, 1),   # the longest lists the tail launch takes: their union fills 256 slots
+    (5, 280, 65, 1),   # one entry longer: a single launch
+    (4, 140, 3, 2),
+])
+def test_bf16_frame_tails_generic_lists(T, P, max_kv, mask_heads):
+    """Blocks of P rows ending in a short tile (block_q == block_k == P), lists
+    with repeated entries (counted twice), entries outside [0, T), empty lists
+    and kv_cnt above max_kv: the tails of four blocks share one walk over the
+    union of their lists, each wave keeping its own list's keys."""
+    torch = _torch()
+    rng = np.random.default_rng(300 + T * P + max_kv)
+    heads, d = 2, 128
+    n = T * P
+    q, k, v = (synth.bf16_round(rng.standard_normal((heads, n, d)).astype(np.float32) * sc) for sc in (1.5, 1.5, 1.0))
+    hm = mask_heads
+    idx = rng.integers(-1, T + 1, size=(hm, T, max_kv)).astype(np.int32)
+    cnt = rng.integers(0, max_kv + 1, size=(hm, T)).astype(np.int32)
+    cnt[0, min(1, T - 1)] = 0
+    cnt[-1, -1] = max_kv + 3
+    if max_kv >= 64:
+        cnt[:, :4] = max_kv
+    note(f"frame tails generic lists T={T} P={P} max_kv={max_kv} mask_heads={hm}")
+    o = to_host(_lib.block_sparse_attn_fwd(to_dev(q), to_dev(k), to_dev(v), P, P, torch.from_numpy(idx).cuda(),
+                                           torch.from_numpy(cnt).cuda(), mask_heads=hm))
+    cnt_o = np.minimum(cnt, max_kv)
+    clean = np.zeros_like(idx)
+    ccnt = np.zeros_like(cnt_o)
+    for h in range(hm):
+        for b in range(T):
+            keep = [x for x in idx[h, b, : cnt_o[h, b]] if 0 <= x < T]
+            clean[h, b, : len(keep)] = keep
+            ccnt[h, b] = len(keep)
+    ref = oracle.block_sparse_attention(q, k, v, P, P, clean, ccnt, mask_heads=hm)
+    assert_attn_close(o, ref, what=f"frame tails T={T} P={P} max_kv={max_kv}")
 
 
 @pytest.mark.parametrize("n,bq,bk,max_kv,mask_heads,sorted_lists", [

@@ -149,6 +149,14 @@ int check_attn(const void* q, const void* k, const void* v, const float* o, int 
 int run_attn(lvsa::AttnArgs& a, int dt, int d, void* stream) {
   const int bm = dt == LVSA_BF16 ? lvsa::kBM_BF16 : lvsa::kBM_F32;
   a.tiles_per_qb = (a.block_q + bm - 1) / bm;
+  // Block lists over blocks that end in a short tile (LVSA frames: 1560 rows
+  // = 12 x 128 + 24): the full tiles in one launch, the short tails of four
+  // consecutive blocks per workgroup in a second one.
+  const int tail = a.block_q % lvsa::kBM_BF16;
+  const bool split = dt == LVSA_BF16 && d == 128 && !a.dense && !a.block_valid && a.block_q == a.block_k &&
+                     a.block_q > lvsa::kBM_BF16 && tail > 0 && tail <= 32 && a.max_kv <= lvsa::kTailMaxKv &&
+                     a.block_k < (1 << 24);
+  if (split) a.tiles_per_qb = a.block_q / lvsa::kBM_BF16;
   const long long total = (long long)a.heads * a.nqb * a.tiles_per_qb;
   if (total >= (1ll << 31)) return fail(LVSA_EINVAL, "too many query tiles (%lld)", total);
   a.total_tiles = (int)total;
@@ -156,6 +164,15 @@ int run_attn(lvsa::AttnArgs& a, int dt, int d, void* stream) {
   int rc = check_device();
   if (rc) return rc;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (split) {
+    hipError_t e = lvsa::launch_attn_bf16(a, d, s);
+    if (e == hipSuccess) {
+      lvsa::AttnArgs t = a;
+      t.total_tiles = (int)((long long)a.heads * ((a.nqb + 3) / 4));
+      e = lvsa::launch_lvsa_tail_bf16(t, s);
+    }
+    return launched(e, "attention launch");
+  }
   // Block lists with per-block valid counts (Draft on reordered tokens) walk
   // only the valid rows of each block.
   const bool grp = dt == LVSA_BF16 && d == 128 && !a.dense && a.block_valid && a.block_q == a.block_k &&

@@ -1,13 +1,22 @@
-// Block-sparse softmax attention forward for Draft Attention's block lists,
-// bf16 in, fp32 out, d = 128, on the gfx950 matrix cores, with a compacted
-// key walk.
+// Block-sparse softmax attention forward with a compacted key walk, bf16 in,
+// fp32 out, d = 128, on the gfx950 matrix cores: Draft Attention's block
+// lists, and the short last tile of LVSA frames.
 //
-// What it computes: Draft Attention's block-sparse execution (the article's
-// block-size and reorder paragraphs): every query row of a query block
-// attends to the valid keys of the KV blocks listed for it, O = softmax(scale
-// * Q Kᵀ) V over those keys only, on the reordered tokens (blocks with
-// per-block valid counts, MODE_GRP) or in place on the raster [t, h, w]
-// layout where a block is a pool tile 16 tokens wide (MODE_T2DG).
+// What it computes: every query row of a query block attends to the valid
+// keys of the KV blocks listed for it, O = softmax(scale * Q Kᵀ) V over those
+// keys only. MODE_GRP and MODE_T2DG: Draft Attention's block-sparse execution
+// (the article's block-size and reorder paragraphs) on the reordered tokens
+// (blocks with per-block valid counts) or in place on the raster [t, h, w]
+// layout where a block is a pool tile 16 tokens wide. MODE_TAIL: the rows of
+// LVSA frames ("LVSA: Training-Free Sparse Attention for Long Video
+// Diffusion", §2: a frame's queries attend to the frames of its attend set)
+// past their last full 128-row tile (24 of the 1560 rows of a Wan frame);
+// the full tiles are the work of bsa_fwd_d128_kernel. A workgroup takes the
+// tails of four consecutive frames, one wave each, and walks the union of
+// their lists once (the lists of neighbouring frames share most entries);
+// each key carries the bits of the waves whose list holds it, and a wave
+// masks the others. A frame's tail alone in a 128-row workgroup cost 6.5 %
+// of the LVSA time for 1.5 % of the rows.
 //
 // Same algorithm, LDS layouts, operand layouts and software pipeline as
 // bsa_fwd_d128_kernel (attn_bf16.hip, whose header describes them), with two
@@ -70,12 +79,23 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_d128_grp_kernel(AttnArgs 
   const int w = blockIdx.x;
   const int xcd = w & 7, idx = w >> 3, q8 = G >> 3, r8 = G & 7;
   const int logical = (xcd < r8 ? xcd * (q8 + 1) : r8 * (q8 + 1) + (xcd - r8) * q8) + idx;
-  const int qt = logical % a.tiles_per_qb;
-  const int rest = logical / a.tiles_per_qb;
-  int qb = rest % a.nqb;
-  const int h = rest / a.nqb;
-  static_assert(MODE == MODE_GRP || MODE == MODE_T2DG, "the compacted walk serves MODE_GRP and MODE_T2DG");
+  static_assert(MODE == MODE_GRP || MODE == MODE_T2DG || MODE == MODE_TAIL, "compacted walk modes only");
   constexpr bool RASTER = MODE == MODE_T2DG;
+  constexpr bool TAIL = MODE == MODE_TAIL;
+  int qt, qb, h;
+  if (TAIL) {
+    // Workgroup = four consecutive query blocks of one head; wave w takes the
+    // tail rows of block 4g + w.
+    const int ng4 = (a.nqb + 3) >> 2;
+    h = logical / ng4;
+    qb = 4 * (logical - h * ng4) + wave;
+    qt = 0;
+  } else {
+    qt = logical % a.tiles_per_qb;
+    const int rest = logical / a.tiles_per_qb;
+    qb = rest % a.nqb;
+    h = rest / a.nqb;
+  }
   if (RASTER) {
     // Raster Draft: consecutive workgroups (one XCD) take the same pool tile
     // of consecutive frames, whose top-k lists share more key blocks than
@@ -87,7 +107,7 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_d128_grp_kernel(AttnArgs 
   const int blk_lo = qb * a.block_q;
   const int blk_end = min(blk_lo + a.block_q, a.n);
   int qlim = a.block_q;
-  if (a.block_valid) {
+  if (!TAIL && a.block_valid) {
     int bv = a.block_valid[qb];
     qlim = bv < 0 ? 0 : (bv < qlim ? bv : qlim);
   }
@@ -110,6 +130,15 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_d128_grp_kernel(AttnArgs 
     active = !SKIP || ((s0 + wave * 32) >> a.lpw) < gq.vh;
     no_queries = (s0 >> a.lpw) >= gq.vh;
   }
+  if (TAIL) {
+    // Rows past the block's last full 128-row tile (at most 32).
+    const int tail_lo = (a.block_q >> 7) << 7;
+    qrow = blk_lo + tail_lo + l32;
+    q_valid = qb < a.nqb && l32 < a.block_q - tail_lo && qrow < a.n;
+    q_in_blk = q_valid;
+    active = qb < a.nqb;
+    no_queries = false;
+  }
 
   const size_t head_off = (size_t)h * (size_t)a.n * D;
   const int head_bytes = a.n * D * 2;
@@ -122,15 +151,68 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_d128_grp_kernel(AttnArgs 
   float* __restrict__ Oh = a.o + head_off;
 
   const int mrow = (a.mask_heads > 1 ? h : 0) * a.nqb + qb;
-  int cnt = a.kv_cnt[mrow];
-  cnt = cnt < 0 ? 0 : (cnt > a.max_kv ? a.max_kv : cnt);
-  const int32_t* const list = a.kv_idx + (size_t)mrow * a.max_kv;
+  int cnt = 0;
+  const int32_t* list = nullptr;
+  if (!TAIL) {
+    cnt = a.kv_cnt[mrow];
+    cnt = cnt < 0 ? 0 : (cnt > a.max_kv ? a.max_kv : cnt);
+    list = a.kv_idx + (size_t)mrow * a.max_kv;
+  }
   // Slot table and the walk's length in groups. Slot info: MODE_GRP the
   // block's valid rows; MODE_T2DG valid columns | valid pool rows << 8
   // (columns <= 64); 0 for an invalid entry or an empty block.
   if (tid == 0) sgroups = 0;
   __syncthreads();
-  {
+  if (TAIL) {
+    // The union of the four lists as a multiset: the r-th occurrence of a
+    // block in any list is one slot, wanted by every wave whose list holds
+    // that block at least r + 1 times (info = valid rows | wave bits << 24).
+    // Slots follow list 0 in its order, then what lists 1, 2, 3 add, in
+    // theirs. Thread t reads entry t % 64 of list t / 64 (max_kv <= 64).
+    int* const raw = reinterpret_cast<int*>(&stab[kGrpMaxSlots / 2]);
+    __shared__ int wcount[4];
+    const int lj = tid >> 6, lp = tid & 63, fj = (qb - wave) + lj;
+    int b = -1;
+    if (fj < a.nqb) {
+      const int row = (a.mask_heads > 1 ? h : 0) * a.nqb + fj;
+      int cj = a.kv_cnt[row];
+      cj = cj < 0 ? 0 : (cj > a.max_kv ? a.max_kv : cj);
+      if (lp < cj) {
+        b = a.kv_idx[(size_t)row * a.max_kv + lp];
+        b = (b < 0 || b >= a.nkb) ? -1 : b;
+      }
+    }
+    raw[tid] = b;
+    __syncthreads();
+    bool own = false;
+    int wbits = 0;
+    if (b >= 0) {
+      int r = 0;
+      for (int pp = 0; pp < lp; ++pp) r += raw[64 * lj + pp] == b;
+      own = true;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        int c = 0;
+        for (int pp = 0; pp < 64; ++pp) c += raw[64 * jj + pp] == b;
+        if (c > r) {
+          wbits |= 1 << jj;
+          if (jj < lj) own = false;
+        }
+      }
+    }
+    const unsigned long long ob = __ballot(own);
+    const int before = __builtin_popcountll(ob & ((1ull << lane) - 1ull));
+    if (lane == 0) wcount[lj] = __builtin_popcountll(ob);
+    __syncthreads();
+    int pos = before;
+    for (int jj = 0; jj < lj; ++jj) pos += wcount[jj];
+    if (own) {
+      const int lim = block_lim(a, b);
+      stab[pos] = make_int2(b * a.block_k, lim > 0 ? (lim | (wbits << 24)) : 0);
+      if (lim > 0) atomicAdd(&sgroups, (lim + 15) >> 4);
+    }
+    cnt = __builtin_amdgcn_readfirstlane(wcount[0] + wcount[1] + wcount[2] + wcount[3]);
+  } else {
     int mine = 0;
     for (int sl = tid; sl < cnt; sl += kThreads) {
       const int b = list[sl];
@@ -200,7 +282,9 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_d128_grp_kernel(AttnArgs 
     for (int j = 0; j < 4; ++j) {
       const bool ok = t.full || dR < t.nv[j];
       dma(Vr, st, 1, j, ok ? vdma : kInvalid, (unsigned)(t.base[j] * D * 2));
-      if (!t.full && dp == 0) ((unsigned char*)kval[st])[16 * j + dR] = ok ? 1 : 0;
+      // per-key flags of a masked tile: 1 for a valid key, or (MODE_TAIL) the
+      // bits of the waves it belongs to
+      if (!t.full && dp == 0) ((unsigned char*)kval[st])[16 * j + dR] = ok ? (TAIL ? t.wm[j] : 1) : 0;
     }
   };
   auto qk = [&](int st, f32x16 (&s)[NKB]) {
@@ -255,7 +339,9 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_d128_grp_kernel(AttnArgs 
   // compacted group sequence.
   // Group cursor: slot gslot (first row or token gbase, info ginfo, gng
   // groups), next group gg; the entry of slot gslot + 1 is read one slot ahead.
-  auto slot_ng = [&](int info) { return MODE == MODE_GRP ? (info + 15) >> 4 : info >> 8; };
+  auto slot_ng = [&](int info) {
+    return MODE == MODE_GRP ? (info + 15) >> 4 : TAIL ? ((info & 0xFFFFFF) + 15) >> 4 : info >> 8;
+  };
   auto rd_slot = [&](int sl) { return sl < cnt ? stab[sl] : make_int2(0, 0); };
   int gslot = 0, gg = 0, gng = 0, gbase = 0, ginfo = 0;
   int2 gpre = rd_slot(0);
@@ -270,6 +356,8 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_d128_grp_kernel(AttnArgs 
     gg = 0;
   };
   gadvance();
+  // MODE_TAIL: bits of the waves that have a frame
+  const int tail_live = TAIL ? (1 << min(4, a.nqb - (qb - wave))) - 1 : 0;
   auto next_tile = [&]() {
     GTile t;
     t.full = 1;
@@ -278,10 +366,15 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_d128_grp_kernel(AttnArgs 
       if (gng == 0) {
         t.base[j] = 0;
         t.nv[j] = 0;
+        if (TAIL) t.wm[j] = 0;
       } else {
         if (MODE == MODE_GRP) {
           t.base[j] = gbase + 16 * gg;
           t.nv[j] = min(16, ginfo - 16 * gg);
+        } else if (TAIL) {
+          t.base[j] = gbase + 16 * gg;
+          t.nv[j] = min(16, (ginfo & 0xFFFFFF) - 16 * gg);
+          t.wm[j] = (unsigned)ginfo >> 24;
         } else {
           t.base[j] = gbase + gg * a.gW;
           t.nv[j] = min(16, ginfo & 255);
@@ -290,6 +383,9 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_d128_grp_kernel(AttnArgs 
       }
       t.full &= (t.nv[j] == 16);
     }
+    // MODE_TAIL: a tile needs the per-wave key masks unless every group is
+    // wanted by every wave that has a frame
+    if (TAIL) t.full = t.full && (t.wm[0] & t.wm[1] & t.wm[2] & t.wm[3]) == tail_live;
     return t;
   };
   GTile tprev;
@@ -307,6 +403,7 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_d128_grp_kernel(AttnArgs 
   if (ntiles > 0 && active) qk(0, s);
   __syncthreads();
 
+  const unsigned wbit = TAIL ? (1u << wave) : 0xffu;  // key flag bits that make a key valid for this wave
   auto step = [&](const int st, f32x16 (&cur)[NKB], f32x16 (&nxt)[NKB]) {
     // K of tile i+2 into the stage of tile i (its K was read last step);
     // V of tile i+1 into the other stage (its V was read last step).
@@ -325,7 +422,7 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_d128_grp_kernel(AttnArgs 
             const unsigned f4 = kval[st][(kb * 32 + 8 * g + 4 * half) >> 2];
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-              if (((f4 >> (8 * i)) & 0xffu) == 0u) cur[kb][4 * g + i] = -INFINITY;
+              if (((f4 >> (8 * i)) & wbit) == 0u) cur[kb][4 * g + i] = -INFINITY;
           }
       }
 
@@ -433,6 +530,12 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_d128_grp_kernel(AttnArgs 
 }
 
 }  // namespace
+
+hipError_t launch_lvsa_tail_bf16(const AttnArgs& a, hipStream_t s) {
+  if (a.total_tiles == 0) return hipSuccess;
+  hipLaunchKernelGGL((bsa_fwd_d128_grp_kernel<MODE_TAIL, true>), dim3(a.total_tiles), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_grp_bf16(const AttnArgs& a, hipStream_t s) {
   if (a.total_tiles == 0) return hipSuccess;

@@ -21,7 +21,7 @@ constexpr float kRescale = 8.0f;            // log2 headroom before the referenc
 constexpr float kSumBf16 = 65536.0f;        // bf16 d = 128: largest lane sum of a tile's probabilities
 constexpr float kSumFp8 = 256.0f;           // FP8: the same, so that every probability is <= 2^8 < 448
 
-enum { MODE_DENSE = 0, MODE_LIST = 1, MODE_SMALL = 2, MODE_T2D = 3, MODE_GRP = 4, MODE_T2DG = 5 };
+enum { MODE_DENSE = 0, MODE_LIST = 1, MODE_SMALL = 2, MODE_T2D = 3, MODE_GRP = 4, MODE_T2DG = 5, MODE_TAIL = 6 };
 
 // Where the BN virtual key rows of one tile live. Uniform across the workgroup.
 // Row r < bnd is physical row base0 + r, row r >= bnd is base1 + r; row r is
@@ -190,7 +190,8 @@ __device__ __forceinline__ TileD stream_tile(const TileStream& ts, const AttnArg
 struct GTile {
   int base[4];  // first physical row of group j
   int nv[4];    // valid rows of group j (0 .. 16)
-  int full;     // every group has 16 valid rows
+  int wm[4];    // MODE_TAIL: bit w set if the keys of group j are keys of wave w
+  int full;     // every group has 16 valid rows (MODE_TAIL: and is wanted by every wave)
 };
 
 // Physical row of tile row r, or -1 if r is not a valid key.

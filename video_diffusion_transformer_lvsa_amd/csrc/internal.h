@@ -56,6 +56,15 @@ hipError_t launch_grp_bf16(const AttnArgs& a, hipStream_t s);
 // Longest key list (max_kv) launch_grp_bf16 accepts: its workgroups hold the
 // list as an LDS table of this many slots.
 constexpr int kGrpMaxSlots = 1024;
+// The last rows of each query block that do not fill a 128-row tile, for
+// lists shared by consecutive blocks (LVSA frames): one workgroup takes the
+// tails of four consecutive blocks, one wave each, and walks the union of
+// their lists once, each wave keeping the keys of its own list. The caller
+// launches the kernels above for the full tiles only (a.tiles_per_qb =
+// block_q / 128). Needs block_q == block_k, block_q % 128 in 1 .. 32, no
+// block_valid, max_kv <= kTailMaxKv; a.total_tiles = heads * ceil(nqb / 4).
+constexpr int kTailMaxKv = 64;
+hipError_t launch_lvsa_tail_bf16(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_f32(const AttnArgs& a, int d, hipStream_t s);
 // E4M3 codes (q, k row-major [heads, n, 128], v transposed [heads, 128, a.ldv])
 // with per-head dequantization factors qs, ks, vs (device arrays).
