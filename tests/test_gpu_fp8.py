@@ -255,13 +255,17 @@ def test_fp8_mfma_block_accumulation():
 
 
 LVSA_FP8 = [
-    # T, H, W, heads, C, window, T_per   (P = H*W, multiples of 4: 64, 100, 1560 run
-    # 4-wave workgroups (128 query rows); 256 and 200 run 8-wave ones (256 rows))
+    # T, H, W, heads, C, window, T_per   (P = H*W, multiples of 4: 64, 100, 1560,
+    # 260, 300 and 384 run 4-wave workgroups (128 query rows); 256 and 200 run
+    # 8-wave ones (256 rows))
     (6, 8, 8, 2, 3, 2, 2),
     (5, 10, 10, 2, 3, 2, 3),
     (12, 30, 52, 2, 5, 3, 4),
     (6, 16, 16, 2, 3, 2, 2),
     (5, 10, 20, 2, 3, 2, 3),
+    (4, 10, 26, 2, 3, 2, 2),
+    (5, 10, 30, 2, 3, 2, 3),
+    (3, 16, 24, 1, 2, 1, 2),
 ]
 
 
@@ -326,6 +330,29 @@ def test_fp8_block_list_edge_cases(k_zero):
                                                       fn=f) for f in (oracle.p_rounding_bound, oracle.attention_p_e4m3))
         slack = oracle.block_sparse_attention(dq, dk, dv, bq, bk, clean, ccnt, mask_heads=heads, scale=0.05, fn=_acc_slack)
         _assert_within_bound(got, ref, bound, model, float(np.abs(dv).max()), "edge lists", slack)
+
+
+@pytest.mark.parametrize("bq", [300, 384])
+def test_fp8_block_lists_long_blocks(bq):
+    """Blocks of 300 rows (three 128-row tiles, the last one 44 rows long) and
+    384 rows (three full tiles), block_q == block_k, a short last block;
+    lists with repeated, skipped and clamped entries, an empty list,
+    per-head lists."""
+    torch = _torch()
+    rng = np.random.default_rng(bq)
+    heads, d, max_kv = 2, 128, 5
+    n = 4 * bq - 60  # a short last block
+    q, k, v = (synth.bf16_round(rng.standard_normal((heads, n, d)).astype(np.float32) * sc) for sc in (2.0, 2.0, 1.0))
+    idx, cnt, clean, ccnt = _edge_lists(rng, heads, n, bq, bq, max_kv)
+    note(f"fp8 long blocks bq={bq}")
+    dev, (dq, dk, dv) = _quant_pair(q, k, v)
+    got = to_host(_run_fp8(dev, bq, bq, torch.from_numpy(idx).cuda(), torch.from_numpy(cnt).cuda(), mask_heads=heads))
+    ref = oracle.block_sparse_attention(dq, dk, dv, bq, bq, clean, ccnt, mask_heads=heads)
+    assert np.all(got[1, bq : 2 * bq] == 0)
+    bound, model = (oracle.block_sparse_attention(dq, dk, dv, bq, bq, clean, ccnt, mask_heads=heads, fn=f)
+                    for f in (oracle.p_rounding_bound, oracle.attention_p_e4m3))
+    slack = oracle.block_sparse_attention(dq, dk, dv, bq, bq, clean, ccnt, mask_heads=heads, fn=_acc_slack)
+    _assert_within_bound(got, ref, bound, model, float(np.abs(dv).max()), f"long blocks bq={bq}", slack)
 
 
 def test_fp8_tiny_scores_stay_finite():
