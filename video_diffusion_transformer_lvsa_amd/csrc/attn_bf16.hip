@@ -45,9 +45,11 @@
 //    fp32 range. d = 64 moves m when the tile max exceeds it by more than
 //    8 (in log2 units).
 //  * Workgroup ids are remapped so that consecutive query tiles (same head,
-//    same query block, same key list) land on the same XCD and share its L2.
-//    Every workgroup of a block walks the same list with the same amount of
-//    work, so they stay in step and the L2 serves most K/V re-reads.
+//    same query block, same key list) land on the same XCD and share its L2,
+//    which then serves most K/V re-reads (96 % hit rate on LVSA lists).
+//  * For LVSA frames (1560 rows = 12 x 128 + 24) the host launches this
+//    kernel over the full 128-row tiles only; the short tails of four frames
+//    per workgroup run in attn_grp.hip (MODE_TAIL).
 //  * MODE_T2D (raster Draft): query and key blocks are pool tiles of the
 //    [t, h, w] grid; a 64-key tile is 64/pool_w pool rows, and a full tile of
 //    16-wide rows loads as four runs of 16 consecutive tokens.

@@ -36,9 +36,9 @@
 //    (measured: 1.5 % slower on the reorder path, 3 % on the raster path).
 //
 // A kernel of its own so that the LVSA and dense launches keep their code:
-// their L2 reuse depends on every workgroup of a frame walking the same list
-// in step, which small changes of the instruction schedule were measured to
-// upset (L2 hit rate 96 % -> 46 % on the 14B LVSA workload).
+// small changes of that kernel's instruction schedule were measured to lower
+// its L2 hit rate on the 14B LVSA workload from 96 % to 46-58 % on most
+// boxes, for reasons not found.
 #include "attn_tiles.h"
 
 namespace lvsa {
