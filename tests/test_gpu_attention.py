@@ -134,21 +134,24 @@ def test_bf16_block_list_edge_cases():
     assert np.all(o[1, bq : 2 * bq] == 0)
 
 
-@pytest.mark.parametrize("T,P,max_kv,mask_heads", [
-    (9, 152, 6, 2),    # per-head lists, groups of 4, 4, 1
-    (5, 280, 64, 1),   # the longest lists the tail launch takes: their union fills 256 slots
-    (5, 280, 65, 1),   # one entry longer: a single launch
-    (4, 140, 3, 2),
+@pytest.mark.parametrize("T,P,max_kv,mask_heads,cut", [
+    (9, 152, 6, 2, 0),    # per-head lists, groups of 4, 4, 1
+    (5, 280, 64, 1, 0),   # the longest lists the tail launch takes: their union fills 256 slots
+    (5, 280, 65, 1, 0),   # one entry longer: a single launch
+    (4, 140, 3, 2, 0),
+    (4, 152, 5, 2, 10),   # last block 142 rows: its tail is 14 of the 24 rows
+    (5, 152, 5, 1, 30),   # last block 122 rows: no tail rows in it
 ])
-def test_bf16_frame_tails_generic_lists(T, P, max_kv, mask_heads):
+def test_bf16_frame_tails_generic_lists(T, P, max_kv, mask_heads, cut):
     """Blocks of P rows ending in a short tile (block_q == block_k == P), lists
     with repeated entries (counted twice), entries outside [0, T), empty lists
     and kv_cnt above max_kv: the tails of four blocks share one walk over the
-    union of their lists, each wave keeping its own list's keys."""
+    union of their lists, each wave keeping its own list's keys; a sequence
+    cut short of T * P rows ends in a shorter last block."""
     torch = _torch()
-    rng = np.random.default_rng(300 + T * P + max_kv)
+    rng = np.random.default_rng(300 + T * P + max_kv + cut)
     heads, d = 2, 128
-    n = T * P
+    n = T * P - cut
     q, k, v = (synth.bf16_round(rng.standard_normal((heads, n, d)).astype(np.float32) * sc) for sc in (1.5, 1.5, 1.0))
     hm = mask_heads
     idx = rng.integers(-1, T + 1, size=(hm, T, max_kv)).astype(np.int32)
@@ -157,7 +160,7 @@ def test_bf16_frame_tails_generic_lists(T, P, max_kv, mask_heads):
     cnt[-1, -1] = max_kv + 3
     if max_kv >= 64:
         cnt[:, :4] = max_kv
-    note(f"frame tails generic lists T={T} P={P} max_kv={max_kv} mask_heads={hm}")
+    note(f"frame tails generic lists T={T} P={P} max_kv={max_kv} mask_heads={hm} n={n}")
     o = to_host(_lib.block_sparse_attn_fwd(to_dev(q), to_dev(k), to_dev(v), P, P, torch.from_numpy(idx).cuda(),
                                            torch.from_numpy(cnt).cuda(), mask_heads=hm))
     cnt_o = np.minimum(cnt, max_kv)
