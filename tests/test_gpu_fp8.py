@@ -266,6 +266,10 @@ LVSA_FP8 = [
     (4, 10, 26, 2, 3, 2, 2),
     (5, 10, 30, 2, 3, 2, 3),
     (3, 16, 24, 1, 2, 1, 2),
+    # frames ending in a short tile (<= 32 rows)
+    (5, 10, 14, 2, 3, 2, 2),   # P = 140 = 128 + 12
+    (7, 8, 20, 2, 4, 2, 3),    # P = 160 = 128 + 32
+    (1, 12, 13, 1, 1, 1, 1),   # P = 156, one frame
 ]
 
 
@@ -353,6 +357,129 @@ def test_fp8_block_lists_long_blocks(bq):
                     for f in (oracle.p_rounding_bound, oracle.attention_p_e4m3))
     slack = oracle.block_sparse_attention(dq, dk, dv, bq, bq, clean, ccnt, mask_heads=heads, fn=_acc_slack)
     _assert_within_bound(got, ref, bound, model, float(np.abs(dv).max()), f"long blocks bq={bq}", slack)
+
+
+def _clean_lists(idx, cnt, nkb):
+    """Lists of valid entries only (repeats kept), as the oracle takes them."""
+    cnt_o = np.minimum(cnt, idx.shape[-1])
+    clean = np.zeros_like(idx)
+    ccnt = np.zeros_like(cnt_o)
+    for h in range(idx.shape[0]):
+        for b in range(idx.shape[1]):
+            keep = [x for x in idx[h, b, : cnt_o[h, b]] if 0 <= x < nkb]
+            clean[h, b, : len(keep)] = keep
+            ccnt[h, b] = len(keep)
+    return clean, ccnt
+
+
+def _check_fp8_lists(got, dq, dk, dv, bq, bk, clean, ccnt, hm, what, block_valid=None):
+    kw = dict(mask_heads=hm, block_valid=block_valid)
+    ref = oracle.block_sparse_attention(dq, dk, dv, bq, bk, clean, ccnt, **kw)
+    bound, model = (oracle.block_sparse_attention(dq, dk, dv, bq, bk, clean, ccnt, fn=f, **kw)
+                    for f in (oracle.p_rounding_bound, oracle.attention_p_e4m3))
+    slack = oracle.block_sparse_attention(dq, dk, dv, bq, bk, clean, ccnt, fn=_acc_slack, **kw)
+    _assert_within_bound(got, ref, bound, model, float(np.abs(dv).max()), what, slack)
+
+
+@pytest.mark.parametrize("block,seed", [(128, 0), (64, 1), (192, 2)])
+def test_fp8_block_valid_edge_cases(block, seed):
+    """FP8 block lists over blocks with per-block valid counts: valid counts
+    0, 1, 15, 16, 17, 63, 64, a full block and others (partly valid groups of
+    4 keys), repeated, negative and out-of-range entries, empty lists, counts
+    above max_kv; pad query rows give 0."""
+    torch = _torch()
+    rng = np.random.default_rng(170 + seed)
+    heads, d, nb, max_kv = 2, 128, 12, 7
+    n = nb * block
+    q, k, v = (synth.bf16_round(rng.standard_normal((heads, n, d)).astype(np.float32) * sc) for sc in (1.5, 1.5, 1.0))
+    special = [0, 1, 15, 16, 17, 63, 64, block, block - 1, 33, 100 % block, 48]
+    bv = np.array(special[:nb], dtype=np.int32)
+    rng.shuffle(bv)
+    idx = rng.integers(-1, nb + 1, size=(heads, nb, max_kv)).astype(np.int32)
+    cnt = rng.integers(0, max_kv + 1, size=(heads, nb)).astype(np.int32)
+    idx[0, 0, :3] = idx[0, 0, 0]
+    cnt[0, 1] = 0
+    cnt[1, 2] = max_kv + 5
+    idx[1, 3, :] = np.argsort(bv)[:max_kv]
+    cnt[1, 3] = max_kv
+    note(f"fp8 block_valid edge cases block={block}")
+    dev, (dq, dk, dv) = _quant_pair(q, k, v)
+    got = to_host(_lib.block_sparse_attn_fwd_fp8(dev["q8"], dev["k8"], dev["vt8"], dev["q_scale"], dev["k_scale"],
+                                                 dev["v_scale"], block, block, torch.from_numpy(idx).cuda(),
+                                                 torch.from_numpy(cnt).cuda(), mask_heads=heads,
+                                                 block_valid=torch.from_numpy(bv).cuda()))
+    clean, ccnt = _clean_lists(idx, cnt, nb)
+    for b in range(nb):
+        assert np.all(got[:, b * block + bv[b] : (b + 1) * block] == 0)  # pad query rows
+    _check_fp8_lists(got, dq, dk, dv, block, block, clean, ccnt, heads, f"fp8 block_valid edge block={block}", block_valid=bv)
+
+
+@pytest.mark.parametrize("T,P,max_kv,mask_heads,cut", [
+    (9, 152, 6, 2, 0),    # per-head lists, frame groups of 4, 4, 1
+    (5, 280, 64, 1, 0),   # the longest lists the tail launch takes
+    (5, 280, 65, 1, 0),   # one entry longer: one launch
+    (4, 152, 5, 2, 8),    # last block 144 rows: its tail is 16 of the 24 rows
+])
+def test_fp8_short_last_tile_generic_lists(T, P, max_kv, mask_heads, cut):
+    """FP8 blocks of P rows ending in a short tile (block_q == block_k == P),
+    a short last block: lists with repeated, invalid and clamped entries, an
+    empty list, per-head lists, 64- and 65-entry lists."""
+    torch = _torch()
+    rng = np.random.default_rng(400 + T * P + max_kv + cut)
+    heads, d = 2, 128
+    n = T * P - cut
+    q, k, v = (synth.bf16_round(rng.standard_normal((heads, n, d)).astype(np.float32) * sc) for sc in (1.5, 1.5, 1.0))
+    hm = mask_heads
+    idx = rng.integers(-1, T + 1, size=(hm, T, max_kv)).astype(np.int32)
+    cnt = rng.integers(0, max_kv + 1, size=(hm, T)).astype(np.int32)
+    cnt[0, min(1, T - 1)] = 0
+    cnt[-1, -1] = max_kv + 3
+    if max_kv >= 64:
+        cnt[:, :4] = max_kv
+    note(f"fp8 short last tiles T={T} P={P} max_kv={max_kv} mask_heads={hm} n={n}")
+    dev, (dq, dk, dv) = _quant_pair(q, k, v)
+    got = to_host(_run_fp8(dev, P, P, torch.from_numpy(idx).cuda(), torch.from_numpy(cnt).cuda(), mask_heads=hm))
+    clean, ccnt = _clean_lists(idx, cnt, T)
+    _check_fp8_lists(got, dq, dk, dv, P, P, clean, ccnt, hm, f"fp8 short last tiles T={T} P={P} max_kv={max_kv}")
+
+
+@pytest.mark.parametrize("path,max_kv", [("reorder", 1024), ("reorder", 1025), ("raster", 1024), ("raster", 1025)])
+def test_fp8_long_draft_lists(path, max_kv):
+    """FP8 key lists of 1024 and 1025 entries (the longest the bf16 compacted
+    walk's slot table holds, and one more) with repeated and invalid
+    entries, short and empty lists, on both Draft paths."""
+    torch = _torch()
+    rng = np.random.default_rng(190 + (max_kv & 1) + (2 if path == "raster" else 0))
+    heads, d = 1, 128
+    if path == "reorder":
+        block, nb = 64, 8
+        n = nb * block
+        bv = np.array([64, 48, 64, 4, 64, 20, 64, 32], dtype=np.int32)
+    else:
+        T, H, W, ph, pw = 1, 16, 24, 8, 16
+        g = oracle.draft_grid(T, H, W, ph, pw)
+        perm, inv, bv = oracle.draft_permutation(g)
+        n, nb = T * H * W, g.nb
+    q, k, v = (synth.bf16_round(rng.standard_normal((heads, n, d)).astype(np.float32) * sc) for sc in (1.5, 1.5, 1.0))
+    idx = rng.integers(-1, nb + 1, size=(heads, nb, max_kv)).astype(np.int32)
+    lens = [max_kv, 0, max_kv - 3, 5, 1, max_kv // 2, 2, max_kv]
+    cnt = np.array([lens[:nb]], dtype=np.int32)
+    note(f"fp8 long lists path={path} max_kv={max_kv}")
+    dev, (dq, dk, dv) = _quant_pair(q, k, v)
+    args = (dev["q8"], dev["k8"], dev["vt8"], dev["q_scale"], dev["k_scale"], dev["v_scale"])
+    ti, tc = torch.from_numpy(idx).cuda(), torch.from_numpy(cnt).cuda()
+    clean, ccnt = _clean_lists(idx, cnt, nb)
+    if path == "reorder":
+        got = to_host(_lib.block_sparse_attn_fwd_fp8(*args, block, block, ti, tc, mask_heads=heads,
+                                                     block_valid=torch.from_numpy(bv).cuda()))
+        _check_fp8_lists(got, dq, dk, dv, block, block, clean, ccnt, heads, f"fp8 long lists {path} {max_kv}",
+                         block_valid=bv)
+    else:
+        got = to_host(_lib.draft_attn_fwd_fp8(*args, T, H, W, ph, pw, ti, tc))
+        ref, bound, model, slack = (oracle.draft_attention_original_order(dq, dk, dv, perm, inv, bv, g.block_size,
+                                                                          clean, ccnt, fn=f)
+                                    for f in (None, oracle.p_rounding_bound, oracle.attention_p_e4m3, _acc_slack))
+        _assert_within_bound(got, ref, bound, model, float(np.abs(dv).max()), f"fp8 long lists {path} {max_kv}", slack)
 
 
 def test_fp8_tiny_scores_stay_finite():
