@@ -136,8 +136,9 @@ def test_bf16_block_list_edge_cases():
 
 @pytest.mark.parametrize("T,P,max_kv,mask_heads,cut", [
     (9, 152, 6, 2, 0),    # per-head lists, groups of 4, 4, 1
-    (5, 280, 64, 1, 0),   # the longest lists the tail launch takes: their union fills 256 slots
-    (5, 280, 65, 1, 0),   # one entry longer: a single launch
+    (5, 280, 64, 1, 0),
+    (5, 280, 128, 1, 0),  # the longest lists the tail launch takes: their union fills 512 slots
+    (5, 280, 129, 1, 0),  # one entry longer: a single launch
     (4, 140, 3, 2, 0),
     (4, 152, 5, 2, 10),   # last block 142 rows: its tail is 14 of the 24 rows
     (5, 152, 5, 1, 30),   # last block 122 rows: no tail rows in it

@@ -168,50 +168,71 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_d128_grp_kernel(AttnArgs 
     // block in any list is one slot, wanted by every wave whose list holds
     // that block at least r + 1 times (info = valid rows | wave bits << 24).
     // Slots follow list 0 in its order, then what lists 1, 2, 3 add, in
-    // theirs. Thread t reads entry t % 64 of list t / 64 (max_kv <= 64).
-    int* const raw = reinterpret_cast<int*>(&stab[kGrpMaxSlots / 2]);
-    __shared__ int wcount[4];
-    const int lj = tid >> 6, lp = tid & 63, fj = (qb - wave) + lj;
-    int b = -1;
+    // theirs. Wave w reads list w, lane l its entries l and l + 64
+    // (max_kv <= kTailMaxKv = 128: at most 512 slots, below the raw lists).
+    int* const raw = reinterpret_cast<int*>(&stab[kGrpMaxSlots / 2]);  // [4][128]
+    __shared__ int wcount[4][2];
+    const int lj = tid >> 6, fj = (qb - wave) + lj;
+    int cj = 0;
     if (fj < a.nqb) {
-      const int row = (a.mask_heads > 1 ? h : 0) * a.nqb + fj;
-      int cj = a.kv_cnt[row];
+      cj = a.kv_cnt[(a.mask_heads > 1 ? h : 0) * a.nqb + fj];
       cj = cj < 0 ? 0 : (cj > a.max_kv ? a.max_kv : cj);
+    }
+    const int32_t* const lst = a.kv_idx + (size_t)((a.mask_heads > 1 ? h : 0) * a.nqb + fj) * a.max_kv;
+    int bb[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int lp = lane + 64 * e;
+      int b = -1;
       if (lp < cj) {
-        b = a.kv_idx[(size_t)row * a.max_kv + lp];
+        b = lst[lp];
         b = (b < 0 || b >= a.nkb) ? -1 : b;
       }
+      raw[128 * lj + lp] = b;
+      bb[e] = b;
     }
-    raw[tid] = b;
     __syncthreads();
-    bool own = false;
-    int wbits = 0;
-    if (b >= 0) {
-      int r = 0;
-      for (int pp = 0; pp < lp; ++pp) r += raw[64 * lj + pp] == b;
-      own = true;
+    bool own[2];
+    int wbits[2];
+    unsigned long long ob[2];
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        int c = 0;
-        for (int pp = 0; pp < 64; ++pp) c += raw[64 * jj + pp] == b;
-        if (c > r) {
-          wbits |= 1 << jj;
-          if (jj < lj) own = false;
+    for (int e = 0; e < 2; ++e) {
+      const int lp = lane + 64 * e, b = bb[e];
+      own[e] = false;
+      wbits[e] = 0;
+      if (b >= 0) {
+        int r = 0;
+        for (int pp = 0; pp < lp; ++pp) r += raw[128 * lj + pp] == b;
+        own[e] = true;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          int c = 0;
+          for (int pp = 0; pp < 128; ++pp) c += raw[128 * jj + pp] == b;
+          if (c > r) {
+            wbits[e] |= 1 << jj;
+            if (jj < lj) own[e] = false;
+          }
         }
       }
+      ob[e] = __ballot(own[e]);
+      if (lane == 0) wcount[lj][e] = __builtin_popcountll(ob[e]);
     }
-    const unsigned long long ob = __ballot(own);
-    const int before = __builtin_popcountll(ob & ((1ull << lane) - 1ull));
-    if (lane == 0) wcount[lj] = __builtin_popcountll(ob);
     __syncthreads();
-    int pos = before;
-    for (int jj = 0; jj < lj; ++jj) pos += wcount[jj];
-    if (own) {
-      const int lim = block_lim(a, b);
-      stab[pos] = make_int2(b * a.block_k, lim > 0 ? (lim | (wbits << 24)) : 0);
-      if (lim > 0) atomicAdd(&sgroups, (lim + 15) >> 4);
+    int pos0 = 0;
+    for (int jj = 0; jj < lj; ++jj) pos0 += wcount[jj][0] + wcount[jj][1];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      if (own[e]) {
+        const int pos = pos0 + (e ? wcount[lj][0] : 0) + __builtin_popcountll(ob[e] & ((1ull << lane) - 1ull));
+        const int lim = block_lim(a, bb[e]);
+        stab[pos] = make_int2(bb[e] * a.block_k, lim > 0 ? (lim | (wbits[e] << 24)) : 0);
+        if (lim > 0) atomicAdd(&sgroups, (lim + 15) >> 4);
+      }
     }
-    cnt = __builtin_amdgcn_readfirstlane(wcount[0] + wcount[1] + wcount[2] + wcount[3]);
+    int total = 0;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) total += wcount[jj][0] + wcount[jj][1];
+    cnt = __builtin_amdgcn_readfirstlane(total);
   } else {
     int mine = 0;
     for (int sl = tid; sl < cnt; sl += kThreads) {

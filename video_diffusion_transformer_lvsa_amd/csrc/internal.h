@@ -63,7 +63,7 @@ constexpr int kGrpMaxSlots = 1024;
 // launches the kernels above for the full tiles only (a.tiles_per_qb =
 // block_q / 128). Needs block_q == block_k, block_q % 128 in 1 .. 32, no
 // block_valid, max_kv <= kTailMaxKv; a.total_tiles = heads * ceil(nqb / 4).
-constexpr int kTailMaxKv = 64;
+constexpr int kTailMaxKv = 128;
 hipError_t launch_lvsa_tail_bf16(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_f32(const AttnArgs& a, int d, hipStream_t s);
 // E4M3 codes (q, k row-major [heads, n, 128], v transposed [heads, 128, a.ldv])
