@@ -42,7 +42,7 @@ ATTN_GRP_SRC = os.path.join(ROOT, "video_diffusion_transformer_lvsa_amd", "csrc"
 # (attn_bf16.hip) and then the short frame tails, four frames per workgroup
 # (attn_grp.hip).
 LVSA_SRCS = (ATTN_SRC, ATTN_GRP_SRC)
-LVSA_KERNELS = ("bsa_fwd_d128_kernel<MODE_LIST, false>", "bsa_fwd_d128_grp_kernel<MODE_TAIL, true>")
+LVSA_KERNELS = ("bsa_fwd_d128_kernel<MODE_LIST, false, 8>", "bsa_fwd_d128_grp_kernel<MODE_TAIL, true>")
 DRAFT_SRC = os.path.join(ROOT, "video_diffusion_transformer_lvsa_amd", "csrc", "draft.hip")
 
 WORKLOAD_NAMES = {
@@ -627,7 +627,7 @@ def _profiled_kernel(workload: str, fp8: bool, raster: bool = False):
         tmpl, label = (("bsa_fwd_d128_grp_kernel<5, false>", "bsa_fwd_d128_grp_kernel<MODE_T2DG, false>") if raster
                        else ("bsa_fwd_d128_grp_kernel<4, true>", "bsa_fwd_d128_grp_kernel<MODE_GRP, true>"))
         return (ATTN_GRP_SRC,), tmpl, label, key, alg, ()
-    return LVSA_SRCS, "bsa_fwd_d128_kernel<1, false>", LVSA_KERNELS[0], key, alg, ("bsa_fwd_d128_grp_kernel<6, true>",)
+    return LVSA_SRCS, "bsa_fwd_d128_kernel<1, false, 8>", LVSA_KERNELS[0], key, alg, ("bsa_fwd_d128_grp_kernel<6, true>",)
 
 
 def summarize(argv) -> int:

@@ -17,7 +17,7 @@ import bench  # noqa: E402
 COLS = ["Correlation_Id", "Dispatch_Id", "Agent_Id", "Queue_Id", "Process_Id", "Thread_Id", "Grid_Size", "Kernel_Id",
         "Kernel_Name", "Workgroup_Size", "LDS_Block_Size", "Scratch_Size", "VGPR_Count", "Accum_VGPR_Count",
         "SGPR_Count", "Counter_Name", "Counter_Value", "Start_Timestamp", "End_Timestamp"]
-ATTN = "void lvsa::(anonymous namespace)::bsa_fwd_d128_kernel<1, false>(lvsa::AttnArgs)"
+ATTN = "void lvsa::(anonymous namespace)::bsa_fwd_d128_kernel<1, false, 8>(lvsa::AttnArgs)"
 TAIL = "void lvsa::(anonymous namespace)::bsa_fwd_d128_grp_kernel<6, true>(lvsa::AttnArgs)"
 COPY = "void lvsa::(anonymous namespace)::token_permute_kernel(u32x4 const*, u32x4*, int const*, int, int, int)"
 

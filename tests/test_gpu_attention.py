@@ -80,6 +80,9 @@ SMALL_LVSA = [
     (1, 12, 13, 1, 128, 1, 1, 1),   # P = 156, one frame
     (6, 11, 12, 2, 128, 6, 3, 2),   # P = 132 = 128 + 4, every frame listed
     (3, 10, 17, 1, 128, 2, 1, 2),   # P = 170 = 128 + 42: tail longer than a wave, one launch
+    # an even number of full tiles: they run as 256-row workgroups of eight waves
+    (5, 16, 17, 2, 128, 3, 2, 2),   # P = 272 = 256 + 16
+    (6, 20, 27, 1, 128, 3, 2, 2),   # P = 540 = 2 x 256 + 28, two eight-wave workgroups per frame
 ]
 
 
@@ -142,6 +145,10 @@ def test_bf16_block_list_edge_cases():
     (4, 140, 3, 2, 0),
     (4, 152, 5, 2, 10),   # last block 142 rows: its tail is 14 of the 24 rows
     (5, 152, 5, 1, 30),   # last block 122 rows: no tail rows in it
+    # full tiles as 256-row workgroups of eight waves
+    (6, 536, 8, 2, 0),    # 2 x 256 + 24
+    (5, 280, 6, 1, 100),  # last block 180 rows: its workgroup holds 76 rows past the end
+    (5, 536, 6, 1, 300),  # last block 236 rows: its second workgroup lies wholly past the end
 ])
 def test_bf16_frame_tails_generic_lists(T, P, max_kv, mask_heads, cut):
     """Blocks of P rows ending in a short tile (block_q == block_k == P), lists

@@ -156,7 +156,14 @@ int run_attn(lvsa::AttnArgs& a, int dt, int d, void* stream) {
   const bool split = dt == LVSA_BF16 && d == 128 && !a.dense && !a.block_valid && a.block_q == a.block_k &&
                      a.block_q > lvsa::kBM_BF16 && tail > 0 && tail <= 32 && a.max_kv <= lvsa::kTailMaxKv &&
                      a.block_k < (1 << 24);
-  if (split) a.tiles_per_qb = a.block_q / lvsa::kBM_BF16;
+  // Dense d = 128 bf16 attention, and blocks of an even number of full
+  // 128-row tiles, run as 256-row workgroups of eight waves (each K/V tile in
+  // LDS serves twice the query rows).
+  const int waves = dt == LVSA_BF16 && d == 128 && (a.dense || (split && (a.block_q / lvsa::kBM_BF16) % 2 == 0)) ? 8 : 4;
+  if (split)
+    a.tiles_per_qb = a.block_q / (32 * waves);
+  else if (waves == 8)
+    a.tiles_per_qb = (a.block_q + 255) / 256;
   const long long total = (long long)a.heads * a.nqb * a.tiles_per_qb;
   if (total >= (1ll << 31)) return fail(LVSA_EINVAL, "too many query tiles (%lld)", total);
   a.total_tiles = (int)total;
@@ -165,7 +172,7 @@ int run_attn(lvsa::AttnArgs& a, int dt, int d, void* stream) {
   if (rc) return rc;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (split) {
-    hipError_t e = lvsa::launch_attn_bf16(a, d, s);
+    hipError_t e = lvsa::launch_attn_bf16(a, d, s, waves);
     if (e == hipSuccess) {
       lvsa::AttnArgs t = a;
       t.total_tiles = (int)((long long)a.heads * ((a.nqb + 3) / 4));
@@ -178,7 +185,7 @@ int run_attn(lvsa::AttnArgs& a, int dt, int d, void* stream) {
   const bool grp = dt == LVSA_BF16 && d == 128 && !a.dense && a.block_valid && a.block_q == a.block_k &&
                    a.block_k >= 64 && a.block_k % 16 == 0 && a.max_kv <= lvsa::kGrpMaxSlots;
   hipError_t e = grp ? lvsa::launch_grp_bf16(a, s)
-                     : (dt == LVSA_BF16 ? lvsa::launch_attn_bf16(a, d, s) : lvsa::launch_attn_f32(a, d, s));
+                     : (dt == LVSA_BF16 ? lvsa::launch_attn_bf16(a, d, s, waves) : lvsa::launch_attn_f32(a, d, s));
   return launched(e, "attention launch");
 }
 

@@ -8,7 +8,8 @@
 // query row attends to the rows of the KV blocks listed for its query block,
 // O = softmax(scale * Q Kᵀ) V over those keys only.
 //
-// Design (one workgroup = 4 waves = 128 query rows; one wave = 32 rows):
+// Design (one workgroup = 4 waves = 128 query rows, or for d = 128 lists and
+// dense attention 8 waves = 256 rows; one wave = 32 rows):
 //  * The KV list of a query block is walked as one "virtual" key sequence:
 //    list slot i covers virtual rows [i*block_k, (i+1)*block_k). Tiles of
 //    BN virtual rows are gathered row by row, so a frame list of 21 frames
@@ -46,10 +47,16 @@
 //    8 (in log2 units).
 //  * Workgroup ids are remapped so that consecutive query tiles (same head,
 //    same query block, same key list) land on the same XCD and share its L2,
-//    which then serves most K/V re-reads (96 % hit rate on LVSA lists).
+//    which then serves most K/V re-reads (95-96 % hit rate on LVSA lists).
 //  * For LVSA frames (1560 rows = 12 x 128 + 24) the host launches this
-//    kernel over the full 128-row tiles only; the short tails of four frames
-//    per workgroup run in attn_grp.hip (MODE_TAIL).
+//    kernel over the full rows only, as six 256-row workgroups of eight
+//    waves per frame (each K/V tile loaded into LDS serves 256 query rows,
+//    half the L2-to-LDS bytes per FLOP of 128-row workgroups); the short
+//    tails of four frames per workgroup run in attn_grp.hip (MODE_TAIL).
+//    In an eight-wave workgroup the two waves of a SIMD meet at the same
+//    barriers, so the upper four waves issue their Sᵀ MFMAs before their
+//    softmax instead of interleaving them: the VALU work of one wave then
+//    lines up with the MFMAs of the other.
 //  * MODE_T2D (raster Draft): query and key blocks are pool tiles of the
 //    [t, h, w] grid; a 64-key tile is 64/pool_w pool rows, and a full tile of
 //    16-wide rows loads as four runs of 16 consecutive tokens.
@@ -402,9 +409,15 @@ typedef __attribute__((address_space(3))) unsigned char lds_u8;
 // blocks) skip the math but still take their share of the loads and every
 // barrier. Only instantiated for launches with per-block valid counts: the
 // extra branch splits the loop body and costs the list walk some overlap.
-template <int MODE, bool SKIP>
-__global__ __launch_bounds__(kThreads, 2) void bsa_fwd_d128_kernel(AttnArgs a) {
+// NW: waves per workgroup (32 query rows each). Four waves run two
+// workgroups per CU; eight waves run one, and each K/V tile loaded into LDS
+// then serves 256 query rows instead of 128.
+template <int MODE, bool SKIP, int NW = 4>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void bsa_fwd_d128_kernel(AttnArgs a) {
+  static_assert(NW == 4 || (NW == 8 && (MODE == MODE_LIST || MODE == MODE_DENSE)), "eight waves: list or dense");
   constexpr int D = 128, BN = 64, KSTEPS = 8, NKB = 2, PVSTEPS = 4, NDB = 4;
+  constexpr int BM = 32 * NW;      // query rows per workgroup
+  constexpr int NJ = BN / 4 / NW;  // DMA instructions per wave per K or V tile
   constexpr int TILE = BN * D * 2;  // 16 KB per K or V tile
   // Four separate LDS objects (K and V of two stages) so the compiler can see
   // that reading one stage does not wait for the loads filling the other.
@@ -446,7 +459,7 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_d128_kernel(AttnArgs a) {
     qlim = bv < 0 ? 0 : (bv < qlim ? bv : qlim);
   }
   const int qend = min(blk_lo + qlim, blk_end);
-  const int row_lo = blk_lo + qt * kBM;
+  const int row_lo = blk_lo + qt * BM;
   int qrow = row_lo + wave * 32 + l32;
   bool active = !SKIP || row_lo + wave * 32 < qend;
   bool q_in_blk = qrow < blk_end;
@@ -455,7 +468,7 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_d128_kernel(AttnArgs a) {
   if (MODE == MODE_T2D) {
     // Query block qb is a raster pool tile; slot s = (s / pw, s % pw).
     const BlkGeom gq = blk_geom(a, qb);
-    const int s0 = qt * kBM;
+    const int s0 = qt * BM;
     const int slot = s0 + wave * 32 + l32;
     const int hi = slot >> a.lpw, wi = slot & (a.pw - 1);
     q_valid = slot < a.block_q && hi < gq.vh && wi < gq.vw;
@@ -495,8 +508,8 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_d128_kernel(AttnArgs a) {
     qreg[kk] = __builtin_bit_cast(bf16x8, bload(Qr, off));
   }
 
-  // DMA roles: instruction j of wave `wave` fills tile rows 16j + 4*wave .. +3;
-  // lane writes row 16j + dR, LDS chunk dp.
+  // DMA roles: instruction j of wave `wave` fills tile rows 4*NW*j + 4*wave
+  // .. +3; lane writes row 4*NW*j + dR, LDS chunk dp.
   const int dR = 4 * wave + (lane >> 4);
   const int dp = lane & 15;
   const unsigned kdma = (unsigned)(dR * 256 + 16 * (dp ^ (dR & 15)));
@@ -522,20 +535,20 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_d128_kernel(AttnArgs a) {
   auto simple = [&](const TileD& t) {
     return MODE == MODE_T2D ? (t.full && a.pw == 16) : (t.full && (t.bnd >= BN || t.base1 == t.base0));
   };
-  const unsigned run_bytes = MODE == MODE_T2D ? (unsigned)a.gW * D * 2 : 4096u;
+  const unsigned run_bytes = MODE == MODE_T2D ? (unsigned)a.gW * D * 2 : 1024u * NW;
   auto dma = [&](__amdgpu_buffer_rsrc_t r, int st, int kind, int j, unsigned voff, unsigned soff) {
-    unsigned char* dst = (kind == 0 ? kbuf(st) : vbuf(st)) + 4096 * j + 1024 * wave;
+    unsigned char* dst = (kind == 0 ? kbuf(st) : vbuf(st)) + 1024 * NW * j + 1024 * wave;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, voff, soff, 0, 0);
   };
   auto load_k = [&](const TileD& t, int st) {
     if (simple(t)) {
       const unsigned so = (unsigned)(t.base0 * D * 2);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) dma(Kr, st, 0, j, kdma, so + run_bytes * j);
+      for (int j = 0; j < NJ; ++j) dma(Kr, st, 0, j, kdma, so + run_bytes * j);
     } else {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int R = 16 * j + dR;
+      for (int j = 0; j < NJ; ++j) {
+        const int R = 4 * NW * j + dR;
         const int p = tile_row<BN, MODE>(a, t, list, cnt, R);
         dma(Kr, st, 0, j, p >= 0 ? (unsigned)(p * 256 + 16 * (dp ^ (R & 15))) : kInvalid, 0u);
       }
@@ -545,11 +558,11 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_d128_kernel(AttnArgs a) {
     if (simple(t)) {
       const unsigned so = (unsigned)(t.base0 * D * 2);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) dma(Vr, st, 1, j, vdma, so + run_bytes * j);
+      for (int j = 0; j < NJ; ++j) dma(Vr, st, 1, j, vdma, so + run_bytes * j);
     } else {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int R = 16 * j + dR;
+      for (int j = 0; j < NJ; ++j) {
+        const int R = 4 * NW * j + dR;
         const int p = tile_row<BN, MODE>(a, t, list, cnt, R);
         dma(Vr, st, 1, j, p >= 0 ? (unsigned)(p * 256 + 16 * (dp ^ gv_swz(R & 3))) : kInvalid, 0u);
         if (dp == 0) ((unsigned char*)kval[st])[R] = p >= 0 ? 1 : 0;
@@ -646,23 +659,39 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_d128_kernel(AttnArgs a) {
           }
       }
 
-      qk(st ^ 1, nxt);
-
       // Probabilities against the running reference mc, with no row max:
       // a lane whose probabilities of this tile sum to more than kSumBf16
       // (or whose row has no reference yet) sends the wave through the
       // exact path, which moves mc to the row max, rescales and recomputes.
       bf16x8 pb[PVSTEPS];
-      float tl = probs(cur, mc, pb);
-      // Interleave the 16 Sᵀ MFMAs with their K reads (kept three ahead) and
-      // the softmax VALU work, which does not depend on them: a wave overlaps
-      // its own VALU work with its MFMAs only where the two are interleaved.
-      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+      float tl;
+      if (NW == 8 && wave >= 4) {
+        // Eight waves: waves w and w + 4 share a SIMD and meet at the same
+        // barriers. The upper four issue their 16 Sᵀ MFMAs first and the
+        // softmax after them, so their VALU work runs beside the PV MFMAs
+        // of the lower four, whose softmax runs beside these MFMAs.
+        qk(st ^ 1, nxt);
+        tl = probs(cur, mc, pb);
+        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if (i < 13) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+        for (int i = 0; i < 16; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (i < 13) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x402, 200, 0);
+      } else {
+        qk(st ^ 1, nxt);
+        tl = probs(cur, mc, pb);
+        // Interleave the 16 Sᵀ MFMAs with their K reads (kept three ahead) and
+        // the softmax VALU work, which does not depend on them: a wave overlaps
+        // its own VALU work with its MFMAs only where the two are interleaved.
+        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (i < 13) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+        }
       }
       if (__ballot(!(tl <= kSumBf16) || mc == -INFINITY) != 0ull) {
         float mx = -INFINITY;
@@ -724,7 +753,7 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_d128_kernel(AttnArgs a) {
     int lid = l32;
     asm volatile("" : "+v"(lid));
     const BlkGeom gq = blk_geom(a, qb);
-    const int slot = qt * kBM + wave * 32 + lid;
+    const int slot = qt * BM + wave * 32 + lid;
     const int hi = slot >> a.lpw, wi = slot & (a.pw - 1);
     q_valid = slot < a.block_q && hi < gq.vh && wi < gq.vw;
     q_in_blk = q_valid;
@@ -763,9 +792,16 @@ hipError_t launch_mode(const AttnArgs& a, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_d128(const AttnArgs& a, hipStream_t s) {
+hipError_t launch_d128(const AttnArgs& a, int waves, hipStream_t s) {
   dim3 grid(a.total_tiles), block(kThreads);
-  if (a.dense)
+  if (waves == 8) {
+    if (a.dense)
+      hipLaunchKernelGGL((bsa_fwd_d128_kernel<MODE_DENSE, false, 8>), grid, dim3(512), 0, s, a);
+    else if (a.block_k >= 64 && !a.block_valid)
+      hipLaunchKernelGGL((bsa_fwd_d128_kernel<MODE_LIST, false, 8>), grid, dim3(512), 0, s, a);
+    else
+      return hipErrorInvalidValue;
+  } else if (a.dense)
     hipLaunchKernelGGL((bsa_fwd_d128_kernel<MODE_DENSE, false>), grid, block, 0, s, a);
   else if (a.block_k >= 64 && a.block_valid)
     hipLaunchKernelGGL((bsa_fwd_d128_kernel<MODE_LIST, true>), grid, block, 0, s, a);
@@ -782,9 +818,10 @@ hipError_t launch_draft_attn_bf16(const AttnArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_attn_bf16(const AttnArgs& a, int d, hipStream_t s) {
+hipError_t launch_attn_bf16(const AttnArgs& a, int d, hipStream_t s, int waves) {
   if (a.total_tiles == 0) return hipSuccess;
-  return d == 128 ? launch_d128(a, s) : launch_mode<64, 128>(a, s);
+  if (waves != 4 && (waves != 8 || d != 128)) return hipErrorInvalidValue;
+  return d == 128 ? launch_d128(a, waves, s) : launch_mode<64, 128>(a, s);
 }
 
 }  // namespace lvsa

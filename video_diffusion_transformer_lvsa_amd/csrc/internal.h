@@ -46,7 +46,9 @@ struct AttnArgs {
 constexpr int kBM_BF16 = 128;
 constexpr int kBM_F32 = 64;
 
-hipError_t launch_attn_bf16(const AttnArgs& a, int d, hipStream_t s);
+// waves = 8 (d = 128; dense, or lists without block_valid): 256 query rows
+// per workgroup, so a.tiles_per_qb = ceil(block_q / 256).
+hipError_t launch_attn_bf16(const AttnArgs& a, int d, hipStream_t s, int waves = 4);
 // Draft attention on the raster layout (d = 128, bf16): a.tile2d = 1.
 hipError_t launch_draft_attn_bf16(const AttnArgs& a, hipStream_t s);
 // d = 128 bf16 attention with the compacted key walk: lists over blocks with
