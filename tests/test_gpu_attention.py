@@ -83,6 +83,7 @@ SMALL_LVSA = [
     # an even number of full tiles: they run as 256-row workgroups of eight waves
     (5, 16, 17, 2, 128, 3, 2, 2),   # P = 272 = 256 + 16
     (6, 20, 27, 1, 128, 3, 2, 2),   # P = 540 = 2 x 256 + 28, two eight-wave workgroups per frame
+    (5, 12, 24, 2, 128, 3, 2, 2),   # P = 288 = 256 + 32: the longest tail
 ]
 
 
@@ -94,7 +95,8 @@ def test_bf16_lvsa_small_all_rows(T, H, W, heads, d, C, win, T_per):
         assert_attn_close(got, ref, what=f"s={s}")
 
 
-@pytest.mark.parametrize("n,heads,d", [(256, 2, 128), (1000, 2, 128), (333, 3, 64), (64, 1, 128), (1, 1, 128), (130, 2, 64)])
+@pytest.mark.parametrize("n,heads,d", [(256, 2, 128), (1000, 2, 128), (333, 3, 64), (64, 1, 128), (1, 1, 128), (130, 2, 64),
+                                      (255, 1, 128), (513, 2, 128)])
 def test_bf16_dense_all_rows(n, heads, d):
     rng = np.random.default_rng(n)
     q, k, v = (synth.bf16_round(rng.standard_normal((heads, n, d)).astype(np.float32) * sc) for sc in (2.0, 2.0, 1.0))
