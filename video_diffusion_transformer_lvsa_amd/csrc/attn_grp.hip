@@ -379,30 +379,46 @@ __global__ __launch_bounds__(kThreads, 2) void bsa_fwd_d128_grp_kernel(AttnArgs 
   gadvance();
   // MODE_TAIL: bits of the waves that have a frame
   const int tail_live = TAIL ? (1 << min(4, a.nqb - (qb - wave))) - 1 : 0;
+  // Group j of the next tile is group g of the current slot.
+  auto group = [&](GTile& t, int j, int g) {
+    if (MODE == MODE_GRP) {
+      t.base[j] = gbase + 16 * g;
+      t.nv[j] = min(16, ginfo - 16 * g);
+    } else if (TAIL) {
+      t.base[j] = gbase + 16 * g;
+      t.nv[j] = min(16, (ginfo & 0xFFFFFF) - 16 * g);
+      t.wm[j] = (unsigned)ginfo >> 24;
+    } else {
+      t.base[j] = gbase + g * a.gW;
+      t.nv[j] = min(16, ginfo & 255);
+    }
+  };
   auto next_tile = [&]() {
     GTile t;
     t.full = 1;
+    if (gng - gg >= 4) {
+      // All four groups from the current slot: no per-group slot test
+      // (measured: Draft 1.6-1.9 % faster than the per-group walk alone).
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (gng == 0) {
-        t.base[j] = 0;
-        t.nv[j] = 0;
-        if (TAIL) t.wm[j] = 0;
-      } else {
-        if (MODE == MODE_GRP) {
-          t.base[j] = gbase + 16 * gg;
-          t.nv[j] = min(16, ginfo - 16 * gg);
-        } else if (TAIL) {
-          t.base[j] = gbase + 16 * gg;
-          t.nv[j] = min(16, (ginfo & 0xFFFFFF) - 16 * gg);
-          t.wm[j] = (unsigned)ginfo >> 24;
-        } else {
-          t.base[j] = gbase + gg * a.gW;
-          t.nv[j] = min(16, ginfo & 255);
-        }
-        if (++gg == gng) gadvance();
+      for (int j = 0; j < 4; ++j) {
+        group(t, j, gg + j);
+        t.full &= (t.nv[j] == 16);
       }
-      t.full &= (t.nv[j] == 16);
+      gg += 4;
+      if (gg == gng) gadvance();
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (gng == 0) {
+          t.base[j] = 0;
+          t.nv[j] = 0;
+          if (TAIL) t.wm[j] = 0;
+        } else {
+          group(t, j, gg);
+          if (++gg == gng) gadvance();
+        }
+        t.full &= (t.nv[j] == 16);
+      }
     }
     // MODE_TAIL: a tile needs the per-wave key masks unless every group is
     // wanted by every wave that has a frame
