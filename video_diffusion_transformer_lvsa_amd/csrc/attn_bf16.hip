@@ -55,8 +55,8 @@
 //    tails of four frames per workgroup run in attn_grp.hip (MODE_TAIL).
 //    In an eight-wave workgroup the two waves of a SIMD meet at the same
 //    barriers, so the upper four waves issue their Sᵀ MFMAs before their
-//    softmax instead of interleaving them: the VALU work of one wave then
-//    lines up with the MFMAs of the other.
+//    softmax instead of interleaving them, and the lower four interleave
+//    one VALU instruction per MFMA instead of four.
 //  * MODE_T2D (raster Draft): query and key blocks are pool tiles of the
 //    [t, h, w] grid; a 64-key tile is 64/pool_w pool rows, and a full tile of
 //    16-wide rows loads as four runs of 16 consecutive tokens.
@@ -685,12 +685,16 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bsa_fwd_d128_kernel(AttnArgs 
         // Interleave the 16 Sᵀ MFMAs with their K reads (kept three ahead) and
         // the softmax VALU work, which does not depend on them: a wave overlaps
         // its own VALU work with its MFMAs only where the two are interleaved.
+        // Four VALU instructions per MFMA with four waves; the lower waves of
+        // an eight-wave workgroup take one (measured: 1.2-1.5 % faster than
+        // four; two and three in between, none or the upper waves' order
+        // slower).
         __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
           if (i < 13) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, NW == 8 ? 1 : 4, 0);
         }
       }
       if (__ballot(!(tl <= kSumBf16) || mc == -INFINITY) != 0ull) {
