@@ -383,14 +383,16 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bsa_fwd_fp8_kernel(AttnArgs a
     // and recomputes.
     float tl = probs(cur, mc, pcur);
     // Interleave the MFMAs (4 of Sᵀ, 4 of PV) with their LDS reads (kept
-    // ahead) and the softmax VALU work, which depends on neither.
+    // ahead) and the softmax VALU work, which depends on neither: six VALU
+    // instructions after each MFMA, the rest after the last one (measured:
+    // 1.6 % faster than twelve on LVSA lists, 0.5 % on Draft lists).
     if constexpr (decltype(with_pv)::value) {
       __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
       for (int g = 0; g < 8; ++g) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         if (g < 6) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
       }
     }
     if (__ballot(!(tl <= kSumFp8) || mc == -INFINITY) != 0ull) {
