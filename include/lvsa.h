@@ -210,9 +210,9 @@ int token_permute(const void* src, void* dst, int dt, int heads, int n_src, int 
  *        token_permute(O_perm -> O, inv_perm).
  * A call may enqueue more than one kernel on `stream` (bf16, d = 128,
  * blocks that end in a tile of 1-32 rows, such as 1560-row frames, and
- * lists of up to 128 entries: the full 128-row tiles, then the short tails
- * of four blocks per workgroup); O is complete once the stream has run past
- * the call.
+ * lists of up to 128 entries: the rows of the full 128-row tiles, then the
+ * short tails of four blocks per workgroup); O is complete once the stream
+ * has run past the call.
  * ------------------------------------------------------------------------ */
 int block_sparse_attn_fwd(const void* q, const void* k, const void* v, float* o, int dt, int heads, int n, int d,
                           int block_q, int block_k, const int32_t* kv_idx, const int32_t* kv_cnt, int max_kv,
